@@ -1,0 +1,178 @@
+"""Pins for the oracle's dispatch: counts, offsets, row layout and payload.
+
+Counts and offsets are pinned by invariants (they sum to T*k, rank sums are block sums of expert
+counts, offsets are the exclusive cumulative sums) and by numpy's bincount/cumsum. The row layout
+is pinned by a hand-worked example (tests/golden/dispatch_worked_example.txt), by brute force
+(nested loops rank -> expert -> token -> slot appending rows) and by numpy's lexsort. The fp8
+payload is pinned by torch's e4m3 conversion of the scaled block and by the quantisation's error
+bounds and special cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_route_03_amd.workloads import ORDER, WORKLOADS, make_inputs, random_topk
+from conftest import golden_lines
+
+
+def _golden_example():
+    d = {}
+    for line in golden_lines("dispatch_worked_example.txt"):
+        key, *vals = line.split()
+        d[key] = [float(v) if "." in v else int(v) for v in vals]
+    return d
+
+
+def _check_layout(d, topk_idx, E, N):
+    T, k = topk_idx.shape
+    R = T * k
+    flat = topk_idx.reshape(-1)
+    cnt, eoff, rcnt, roff = d["expert_counts"], d["expert_offsets"], d["rank_counts"], \
+        d["rank_offsets"]
+    tr, rt = d["token_row"], d["row_token"]
+    assert cnt.sum() == R
+    assert np.array_equal(cnt, np.bincount(flat, minlength=E))
+    assert np.array_equal(eoff, np.concatenate([[0], np.cumsum(cnt)]))
+    assert np.array_equal(rcnt, cnt.reshape(N, E // N).sum(1))
+    assert np.array_equal(roff, np.concatenate([[0], np.cumsum(rcnt)]))
+    assert np.array_equal(roff, eoff[:: E // N])
+    assert np.array_equal(np.sort(tr), np.arange(R))               # a permutation of the rows
+    assert np.array_equal(rt[tr], np.arange(R) // k)               # row_token inverts token_row
+    row_expert = flat[np.argsort(tr)]
+    assert np.all(np.diff(row_expert) >= 0)                        # grouped by expert
+    for e in range(E):                                             # token order inside an expert
+        seg = rt[eoff[e]:eoff[e + 1]]
+        assert np.all(np.diff(seg) >= 0)
+    order = np.lexsort((np.tile(np.arange(k), T), np.repeat(np.arange(T), k), flat))
+    assert np.array_equal(tr[order], np.arange(R))
+
+
+def test_worked_example_golden():
+    g = _golden_example()
+    T, E, k, N = g["T"][0], g["E"][0], g["k"][0], g["N"][0]
+    idx = np.array(g["topk_idx"], np.int32).reshape(T, k)
+    H = 2
+    x = np.array([[t + 1.0, -(t + 1.0)] for t in range(T)], np.float32)
+    d = oracle.dispatch(x, "f32", idx, E, N, "f32")
+    for key in ["expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "token_row",
+                "row_token"]:
+        assert d[key].tolist() == g[key], key
+    y = oracle.experts(d["recv"], "f32", None, d["expert_offsets"], "scale", "f32")
+    w = np.full((T, k), 0.5, np.float32)
+    out = oracle.combine(y, "f32", d["token_row"], w, "f32")
+    assert out.reshape(-1).tolist() == g["out"]
+    assert out.shape == (T, H)
+
+
+def _brute_force_rows(topk_idx, E, N):
+    T, k = topk_idx.shape
+    epr = E // N
+    rows = []   # (token, slot) in row order
+    for r in range(N):
+        for e in range(r * epr, (r + 1) * epr):
+            for t in range(T):
+                for j in range(k):
+                    if topk_idx[t, j] == e:
+                        rows.append((t, j))
+    return rows
+
+
+@pytest.mark.parametrize("T,E,k,N,seed", [(16, 8, 2, 2, 0), (33, 12, 3, 4, 1), (70, 64, 8, 8, 2),
+                                          (5, 4, 4, 1, 3), (9, 6, 1, 6, 4)])
+def test_brute_force_layout(T, E, k, N, seed):
+    idx = random_topk(T, E, k, seed)
+    x = np.random.default_rng(seed).standard_normal((T, 8)).astype(np.float32)
+    d = oracle.dispatch(x, "f32", idx, E, N, "f32")
+    rows = _brute_force_rows(idx, E, N)
+    for row, (t, j) in enumerate(rows):
+        assert d["token_row"][t * k + j] == row
+        assert d["row_token"][row] == t
+        assert np.array_equal(d["recv"][row], x[t])
+    _check_layout(d, idx, E, N)
+
+
+def test_duplicate_expert_in_a_token_is_two_rows():
+    idx = np.array([[1, 1], [0, 1], [1, 0]], np.int32)
+    x = np.arange(6, dtype=np.float32).reshape(3, 2)
+    d = oracle.dispatch(x, "f32", idx, 2, 1, "f32")
+    assert d["expert_counts"].tolist() == [2, 4]
+    # expert 0: (t1,s0), (t2,s1); expert 1: (t0,s0), (t0,s1), (t1,s1), (t2,s0)
+    assert d["row_token"].tolist() == [1, 2, 0, 0, 1, 2]
+    assert d["token_row"].tolist() == [2, 3, 0, 4, 5, 1]
+
+
+def test_zero_tokens():
+    d = oracle.dispatch(np.zeros((0, 16), np.float32), "f32", np.zeros((0, 2), np.int32), 4, 2,
+                        "f32")
+    assert d["expert_counts"].tolist() == [0] * 4
+    assert d["expert_offsets"].tolist() == [0] * 5
+    assert d["rank_offsets"].tolist() == [0] * 3
+
+
+@pytest.mark.parametrize("name", ORDER)
+def test_workload_layout_and_payload(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    idx, _ = oracle.route(inp["logits"], w.k)
+    d = oracle.dispatch(inp["x"], w.x_dtype, idx, w.E, w.N, w.payload)
+    _check_layout(d, idx, w.E, w.N)
+    if w.payload != "fp8_e4m3":
+        assert np.array_equal(d["recv"], inp["x"][d["row_token"]])
+    if name == "skewed":   # the Zipf bias makes expert 0 far hotter than the mean
+        assert d["expert_counts"][0] > 10 * w.T * w.k / w.E
+
+
+def _quantise_ref(x_f32: np.ndarray):
+    """Block-scaled e4m3 via torch: amax/448 scale in fp32, torch's own division and conversion."""
+    t = torch.from_numpy(x_f32).reshape(x_f32.shape[0], -1, 128)
+    amax = t.abs().amax(-1, keepdim=True)
+    s = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
+    q = (t / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.reshape(x_f32.shape).numpy(), s.reshape(x_f32.shape[0], -1).numpy()
+
+
+def test_fp8_payload_decode_fp8():
+    w = WORKLOADS["decode_fp8"]
+    inp = make_inputs(w)
+    idx, _ = oracle.route(inp["logits"], w.k)
+    d = oracle.dispatch(inp["x"], w.x_dtype, idx, w.E, w.N, w.payload)
+    _check_layout(d, idx, w.E, w.N)
+    xf = oracle.bf16_to_f32(inp["x"])
+    q_ref, s_ref = _quantise_ref(xf)
+    assert np.array_equal(d["recv"], q_ref[d["row_token"]])
+    assert np.array_equal(d["recv_scales"], s_ref[d["row_token"]])
+    # the element of largest magnitude in every block encodes +-448 exactly
+    blocks = d["recv"].reshape(w.rows, -1, 128)
+    assert np.all(((blocks & 0x7F) == 0x7E).any(-1))
+    # error bound of the round trip: 2^-4 relative in the normal range, s*2^-10 below it
+    deq = oracle.e4m3_to_f32(d["recv"]).reshape(w.rows, -1, 128).astype(np.float64)
+    s = d["recv_scales"].astype(np.float64)[:, :, None]
+    xr = xf[d["row_token"]].reshape(w.rows, -1, 128).astype(np.float64)
+    err = np.abs(deq * s - xr)
+    bound = np.maximum(np.abs(xr) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 2.0 ** -20)
+    assert np.all(err <= bound)
+
+
+def test_fp8_special_blocks():
+    x = np.zeros((2, 256), np.float32)
+    x[1, :128] = np.linspace(-3, 5, 128, dtype=np.float32)     # block with amax 5
+    x[1, 128] = -1e-30                                          # tiny lone value
+    d = oracle.dispatch(x, "f32", np.array([[0], [1]], np.int32), 2, 1, "fp8_e4m3")
+    assert d["recv_scales"][0].tolist() == [1.0, 1.0]           # zero blocks: scale 1, codes 0
+    assert np.all(d["recv"][0] == 0)
+    assert d["recv_scales"][1, 0] == np.float32(5.0) / np.float32(448.0)
+    assert d["recv"][1, 127] == 0x7E
+    assert d["recv"][1, 128] == 0xFE                            # its own amax: -448
+    assert np.all(d["recv"][1, 129:] == 0)
+
+
+def test_rejects_invalid():
+    x = np.zeros((2, 128), np.float32)
+    with pytest.raises(ValueError):   # expert id out of range
+        oracle.dispatch(x, "f32", np.array([[0], [4]], np.int32), 4, 2, "f32")
+    with pytest.raises(ValueError):   # E not divisible by N
+        oracle.dispatch(x, "f32", np.array([[0], [1]], np.int32), 4, 3, "f32")
+    with pytest.raises(ValueError):   # fp8 needs H % 128 == 0
+        oracle.dispatch(np.zeros((2, 64), np.float32), "f32", np.array([[0], [1]], np.int32), 4,
+                        2, "fp8_e4m3")

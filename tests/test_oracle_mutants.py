@@ -1,0 +1,65 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies oracle/moe_oracle.c into a temporary directory, plants one plausible mistake (a
+reversed tie-break, a dropped renormalisation, a transposed operand, a wrong rounding mode, ...),
+builds it with gcc, and runs the pin tests that should catch it against that build, in a child
+process. The case passes when those pins fail. Nothing here touches the GPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+MUTANTS = {
+    "tie_to_higher_id": ("(l[a] == l[b] && a < b)", "(l[a] == l[b] && a > b)",
+                         "test_oracle_route.py"),
+    "no_renormalisation": ("(float)(p[idx[j]] / kept)", "(float)(p[idx[j]])",
+                           "test_oracle_route.py"),
+    "softmax_sign": ("p[e] = exp((double)l[e] - mx);", "p[e] = exp(mx - (double)l[e]);",
+                     "test_oracle_route.py"),
+    "round_robin_ranks": ("it->rank = it->expert / epr;", "it->rank = it->expert % N;",
+                          "test_oracle_dispatch.py"),
+    "slot_before_token": (
+        "if (a->token != b->token) return a->token < b->token ? -1 : 1;\n"
+        "    if (a->slot != b->slot) return a->slot < b->slot ? -1 : 1;",
+        "if (a->slot != b->slot) return a->slot < b->slot ? -1 : 1;\n"
+        "    if (a->token != b->token) return a->token < b->token ? -1 : 1;",
+        "test_oracle_dispatch.py"),
+    "fnuz_fp8_max": ("amax / 448.0f", "amax / 240.0f", "test_oracle_dispatch.py"),
+    "e4m3_subnormal_edge": ("if (ex < -6) ", "if (ex < -7) ", "test_oracle_formats.py"),
+    "ties_away_from_zero": ("return nearbyint(a / quantum) * quantum;",
+                            "return round(a / quantum) * quantum;", "test_oracle_formats.py"),
+    "bf16_min_exponent": ("round_to_format(a, 8, -126)", "round_to_format(a, 8, -125)",
+                          "test_oracle_formats.py"),
+    "combine_weights_transposed": ("acc += (double)topk_w[t * k + j]",
+                                   "acc += (double)topk_w[j * T + t]", "test_oracle_combine.py"),
+    "combine_slot0_row_only": ("int64_t row = token_row[t * k + j];\n                acc",
+                               "int64_t row = token_row[t * k];\n                acc",
+                               "test_oracle_combine.py"),
+    "rank_offset_off_by_one": ("rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r];",
+                               "rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r] + (r > 0);",
+                               "test_oracle_dispatch.py"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    before, after, target = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) == 1, f"mutation site for {name} not found exactly once"
+    c_path = tmp_path / f"{name}.c"
+    so_path = tmp_path / f"{name}.so"
+    c_path.write_text(src.replace(before, after))
+    subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-shared", "-fPIC",
+                           str(c_path), "-o", str(so_path), "-lm"])
+    env = dict(os.environ, MOE_ORACLE_LIB=str(so_path))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", target)],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1 and "FAILED" in r.stdout, \
+        f"mutant {name} survived {target}:\n{r.stdout[-2000:]}"

@@ -1,0 +1,18 @@
+"""MI355X (gfx950) MoE token routing: top-k routing, dispatch into per-rank receive buffers, and
+weighted combine, as hand-written HIP kernels behind the C ABI of include/moe_route.h.
+
+The binding functions carry the C names; importing them loads libmoe_route.so and fails loudly if
+it has not been built.
+"""
+
+_EXPORTS = ("moe_route_topk", "moe_dispatch_workspace_bytes", "moe_dispatch_layout",
+            "moe_dispatch_pack", "moe_dispatch", "moe_combine", "moe_status_str",
+            "alloc_dispatch_out", "alloc_workspace", "DispatchBuffers", "MoeError")
+
+
+def __getattr__(name):
+    if name in _EXPORTS:
+        from . import _lib
+        _lib.load()
+        return getattr(_lib, name)
+    raise AttributeError(name)

@@ -1,0 +1,159 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE routing, dispatch and combine library.
+ *
+ * The operations are those of Perplexity, "Enabling trillion-parameter models on AWS EFA":
+ *   - routing: a small linear router decides which experts multiply each token ("Introductie");
+ *   - dispatch: receives the tokens and their per-token experts and sends every token to the
+ *     ranks hosting those experts ("Introductie", "MoE all-to-all over EFA"). It counts tokens per
+ *     expert, turns the counts into offsets with a cumulative sum and packs the tokens into
+ *     contiguous per-destination buffers ("Verzend- en ontvangstbuffers", "Dispatch en Combine"),
+ *     optionally as block-scaled fp8 ("Evaluatie / Dispatch/Combine-latentie");
+ *   - combine: brings the processed rows back to their tokens and accumulates their weighted
+ *     average into the output tensor ("Dispatch en Combine").
+ * Here the destination ranks are disjoint row ranges of one receive buffer on one GPU.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument is a DEVICE pointer, except `out` of the dispatch calls, which is a
+ *     HOST pointer to a struct of device pointers. The caller allocates and owns every buffer; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (0 = the null stream); calls return without synchronising.
+ *   - All arguments are validated before any launch. On an error status nothing is enqueued and
+ *     no output is written. MOE_ERR_HIP means a launch failed (hipGetLastError after the launch).
+ *   - Matrices are row-major and dense: [T, E] means T rows of E elements with no padding.
+ *   - Sizes are int32; T * k must stay below 2^31.
+ *   - Kernels never read or write outside the buffers described below, whatever the values in
+ *     topk_idx / token_row: an expert id outside [0, E) or a row outside [0, T*k) is skipped
+ *     (its row is not written, or it contributes nothing). Such inputs break the preconditions
+ *     and leave the affected outputs unspecified.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,     /* bad size, null pointer, inconsistent arguments */
+    MOE_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels handle (dtype, alignment, E) */
+    MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than moe_dispatch_workspace_bytes() */
+    MOE_ERR_HIP = 4          /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum {
+    MOE_F32 = 0,       /* IEEE-754 binary32 */
+    MOE_BF16 = 1,      /* bfloat16 */
+    MOE_FP8_E4M3 = 2   /* OCP e4m3fn (max 448, no infinities), one byte per element */
+} moe_dtype_t;
+
+/* Largest expert count and largest top-k the kernels handle. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 64
+
+/*
+ * moe_route_topk -- top-k expert selection with renormalised softmax weights ("Introductie": the
+ * router picks the experts of every token; the softmax and its renormalisation over the kept
+ * experts are the reading used where the page names no scoring function).
+ *   logits   [T, E] fp32, finite.
+ *   topk_idx [T, k] int32 out: expert ids, largest logit first; equal logits go to the lower id
+ *            (-0.0 and +0.0 are equal).
+ *   topk_w   [T, k] fp32 out: exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k kept experts,
+ *            evaluated in double and rounded once to fp32; they sum to 1 within k * 2^-24.
+ * Requires 1 <= k <= min(E, MOE_MAX_TOPK), 1 <= E <= MOE_MAX_EXPERTS (else MOE_ERR_UNSUPPORTED
+ * for E or k beyond the maxima, MOE_ERR_INVALID otherwise). T = 0 enqueues nothing.
+ */
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                            int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/*
+ * Bytes of device workspace that moe_dispatch / moe_dispatch_layout need for (T, E, k): per-block
+ * expert histograms and per-item ranks. Returns 0 for invalid sizes. The workspace needs no
+ * initialisation and holds nothing the caller uses afterwards.
+ */
+size_t moe_dispatch_workspace_bytes(int32_t T, int32_t E, int32_t k);
+
+/* Dispatch outputs: device pointers, all allocated by the caller. R = T * k. */
+typedef struct {
+    void* recv;              /* [R, H] payload rows (x's format, or e4m3 codes for FP8) */
+    float* recv_scales;      /* [R, H/128] fp32 block scales when the payload is FP8, else NULL */
+    int32_t* expert_counts;  /* [E]   rows routed to each expert */
+    int32_t* expert_offsets; /* [E+1] exclusive cumulative sum of expert_counts; [E] = R */
+    int32_t* rank_counts;    /* [N]   rows received by each destination rank */
+    int32_t* rank_offsets;   /* [N+1] first row of each rank; [N] = R */
+    int32_t* token_row;      /* [R]   row holding (token t, slot j), at index t*k + j */
+    int32_t* row_token;      /* [R]   source token of each row */
+} moe_dispatch_out_t;
+
+/*
+ * moe_dispatch_layout -- the counting half of dispatch ("Verzend- en ontvangstbuffers": every
+ * sender knows all per-expert counts before writing, so writes are contiguous per destination;
+ * "Dispatch en Combine": per-expert token counts, then their cumulative sum gives the offsets).
+ *   topk_idx [T, k] int32 expert ids in [0, E), normally distinct within a token (a repeated id
+ *            is two separate rows).
+ *   n_ranks  N destination ranks; rank r hosts the experts [r*E/N, (r+1)*E/N) (E % N == 0).
+ *   Writes expert_counts, expert_offsets, rank_counts, rank_offsets, token_row and row_token of
+ *   `out` (recv / recv_scales are ignored). Rows are ordered by (rank, expert, token, slot): each
+ *   rank's rows are contiguous, grouped by expert, tokens ascending inside an expert. The result
+ *   is deterministic (no atomics decide a position).
+ *   workspace: device memory of at least moe_dispatch_workspace_bytes(T, E, k) bytes.
+ * T = 0 writes zero counts and offsets.
+ */
+moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                 int32_t n_ranks, const moe_dispatch_out_t* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch_pack -- the packing half of dispatch ("Dispatch en Combine": once the offsets are
+ * known every token is packed into the send buffers; the receiver's copy into the grouped-GEMM
+ * input is merged into the same write here).
+ *   x          [T, H] tokens, x_dtype MOE_F32 or MOE_BF16, 16-byte aligned, H * elem % 16 == 0.
+ *   token_row  [T * k] as written by moe_dispatch_layout.
+ *   payload_dtype == x_dtype: recv[token_row[t*k+j], :] = x[t, :], bytes unchanged.
+ *   payload_dtype == MOE_FP8_E4M3 ("block-scaled fp8-dispatch", read as 1 x 128 blocks): for every
+ *     token and block b of 128 elements, amax = max |x|, s = amax / 448 in fp32 (1 when amax = 0),
+ *     code = e4m3(x / s) rounded to nearest even and saturated to +-448;
+ *     recv [R, H] uint8 codes, recv_scales [R, H/128] fp32 s. Requires H % 128 == 0.
+ *   recv 16-byte aligned, recv_scales 4-byte aligned.
+ */
+moe_status_t moe_dispatch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H,
+                               int32_t k, const int32_t* token_row, moe_dtype_t payload_dtype,
+                               void* recv, float* recv_scales, hipStream_t stream);
+
+/*
+ * moe_dispatch -- moe_dispatch_layout followed by moe_dispatch_pack on the same stream, with the
+ * arguments described there; `out` supplies recv / recv_scales as well.
+ */
+moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H,
+                          const int32_t* topk_idx, int32_t k, int32_t E, int32_t n_ranks,
+                          moe_dtype_t payload_dtype, const moe_dispatch_out_t* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_combine -- weighted sum of the returned rows of every token ("Dispatch en Combine": the
+ * receiver accumulates the rows from its receive buffer into the output tensor; "Introductie":
+ * combine forms their weighted average -- with renormalised weights that is this sum).
+ *   y         [T * k, H] expert outputs, y_dtype MOE_F32 or MOE_BF16, 16-byte aligned.
+ *   token_row [T * k] row of (t, j); topk_w [T, k] fp32 weights.
+ *   out       [T, H] out_dtype MOE_F32 or MOE_BF16, 16-byte aligned:
+ *             out[t, h] = sum_{j<k} w[t, j] * y[token_row[t*k+j], h], accumulated in fp32 in
+ *             slot order (fused multiply-add), rounded to nearest even for bf16.
+ * Requires H % 8 == 0. T = 0 enqueues nothing.
+ */
+moe_status_t moe_combine(const void* y, moe_dtype_t y_dtype, int32_t T, int32_t H, int32_t k,
+                         const int32_t* token_row, const float* topk_w, void* out,
+                         moe_dtype_t out_dtype, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_str(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE routing hot path on one MI355X.
+
+One step = the whole path over one batch already resident in HBM:
+  moe_route_topk -> moe_dispatch_layout -> moe_dispatch_pack -> moe_combine
+on the prefill batch (4096 tokens, hidden 7168 bf16, 384 experts, top-8, 48 destination ranks,
+bf16 payload and output). The expert outputs combine reads are emulated once before timing
+(row * (expert+1)/256), as the grouped GEMM is not part of the path.
+
+Prints ONE JSON line: value = algorithmic HBM bytes of a step / step time (GB/s), ms_per_step =
+µs per layer / 1000, per-kernel times from HIP events on the launch stream, the roofline of the
+dominant kernel, and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine µs/layer and achieved HBM GB/s (% of peak), 1 MI355X"
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill.json")
+HIP_SRC = os.path.join(ROOT, "combine_moe_route_03_amd", "csrc", "moe_route.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="prefill")
+    p.add_argument("--sets", type=int, default=2,
+                   help="buffer sets used in rotation (each set is about 1 GB at prefill)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="host time budget of the CPU-oracle baseline (0 disables it)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run the 1 GiB plain copy kernel (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes each kernel must move (reads + writes of its inputs and outputs, once each)."""
+    T, H, E, k, N, R = w.T, w.H, w.E, w.k, w.N, w.rows
+    xb = 4 if w.x_dtype == "f32" else 2
+    pb = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[w.payload]
+    yb = 4 if w.y_dtype == "f32" else 2
+    ob = 4 if w.out_dtype == "f32" else 2
+    scales = R * (H // 128) * 4 if w.payload == "fp8_e4m3" else 0
+    return {
+        "route": T * E * 4 + R * 8,                                     # logits; ids + weights
+        "layout": R * 4 + R * 8 + (2 * E + 2 * N + 2) * 4,              # ids; maps; counts
+        "pack": T * H * xb + R * H * pb + scales + R * 4,               # x; rows; token_row
+        "combine": R * H * yb + R * 8 + T * H * ob,                     # rows; maps+w; out
+    }
+
+
+class Prepared:
+    """A C entry point with its ctypes arguments built once (launch cost only in the loop)."""
+
+    def __init__(self, fn, *args):
+        self.fn, self.args = fn, args
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"{self.fn.__name__} returned {st}")
+
+
+def make_set(w, inp, dev, moe, torch):
+    """Device buffers of one step and its four prepared launches."""
+    import numpy as np
+    lib = moe.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.c_void_p
+    if w.x_dtype == "bf16":
+        x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x = torch.from_numpy(inp["x"]).to(dev)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    buf = moe.alloc_dispatch_out(w.T, w.H, w.E, w.k, w.N, w.payload, dev)
+    ws = moe.alloc_workspace(w.T, w.E, w.k, dev)
+    out = torch.empty((w.T, w.H), dtype=moe.TORCH_DTYPES[w.out_dtype], device=dev)
+    struct = buf.as_struct()
+    code = moe.DTYPE_CODES
+    s = {"x": x, "logits": logits, "idx": idx, "w": wt, "buf": buf, "ws": ws, "out": out,
+         "struct": struct}
+    s["route"] = Prepared(lib.moe_route_topk, P(logits.data_ptr()), w.T, w.E, w.k,
+                          P(idx.data_ptr()), P(wt.data_ptr()), stream)
+    s["layout"] = Prepared(lib.moe_dispatch_layout, P(idx.data_ptr()), w.T, w.k, w.E, w.N,
+                           ctypes.byref(struct), P(ws.data_ptr()), ws.numel(), stream)
+    s["pack"] = Prepared(lib.moe_dispatch_pack, P(x.data_ptr()), code[w.x_dtype], w.T, w.H, w.k,
+                         P(buf.token_row.data_ptr()), code[w.payload], P(buf.recv.data_ptr()),
+                         P(buf.recv_scales.data_ptr() if buf.recv_scales is not None else 0),
+                         stream)
+    # one untimed pass, then the emulated expert outputs y = row * (expert+1)/256 (or identity)
+    s["route"]()
+    s["layout"]()
+    s["pack"]()
+    torch.cuda.synchronize()
+    counts = buf.expert_counts.long()
+    e_row = torch.repeat_interleave(torch.arange(w.E, device=dev), counts)
+    if w.payload == "fp8_e4m3":
+        val = buf.recv.view(torch.float8_e4m3fn).float() * \
+            buf.recv_scales.repeat_interleave(128, dim=1)
+    else:
+        val = buf.recv.float()
+    if w.experts == "scale":
+        val = val * ((e_row + 1).float() / 256.0)[:, None]
+    y = val.to(moe.TORCH_DTYPES[w.y_dtype]).contiguous()
+    del val
+    s["y"] = y
+    s["combine"] = Prepared(lib.moe_combine, P(y.data_ptr()), code[w.y_dtype], w.T, w.H, w.k,
+                            P(buf.token_row.data_ptr()), P(wt.data_ptr()), P(out.data_ptr()),
+                            code[w.out_dtype], stream)
+    return s
+
+
+def copy_ceiling(torch, gib: float = 1.0, iters: int = 10):
+    """GB/s of the plain 16-byte streaming copy over `gib` GiB (read + write counted)."""
+    from combine_moe_route_03_amd import build as b
+    lib = ctypes.CDLL(b.BENCH_LIB)
+    lib.bench_stream_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p]
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(2):
+        assert lib.bench_stream_copy16(src.data_ptr(), dst.data_ptr(), n, stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        assert lib.bench_stream_copy16(src.data_ptr(), dst.data_ptr(), n, stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    return {"bytes_per_launch": 2 * n, "us": ms * 1e3, "GBps": 2 * n / (ms * 1e-3) / 1e9}
+
+
+def hbm_traffic(kernel_key: str):
+    """Counter-measured HBM bytes per launch from the committed profile, or None when the
+    kernels changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    with open(HIP_SRC, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("source_sha256"):
+            return None
+    k = rec["kernels"].get(kernel_key)
+    if not k:
+        return None
+    return int(round(k["fetch_kib"] * 1024 * rec["copy_calibration"]["read_factor"] +
+                     k["write_kib"] * 1024 * rec["copy_calibration"]["write_factor"]))
+
+
+def cpu_baseline(w, seconds: float, alg_total: int):
+    """The CPU oracle, single-threaded, on the same batch: route + dispatch + combine passes
+    repeated until `seconds` of work have been timed (expert emulation untimed)."""
+    import oracle
+    from combine_moe_route_03_amd.workloads import make_inputs
+    inp = make_inputs(w)
+    idx, wt = oracle.route(inp["logits"], w.k)
+    d = oracle.dispatch(inp["x"], w.x_dtype, idx, w.E, w.N, w.payload)
+    y = oracle.experts(d["recv"], w.payload, d["recv_scales"], d["expert_offsets"], w.experts,
+                       w.y_dtype)
+    del d
+    busy, n = 0.0, 0
+    while busy < seconds or n == 0:
+        t0 = time.perf_counter()
+        idx, wt = oracle.route(inp["logits"], w.k)
+        d = oracle.dispatch(inp["x"], w.x_dtype, idx, w.E, w.N, w.payload)
+        oracle.combine(y, w.y_dtype, d["token_row"], wt, w.out_dtype)
+        busy += time.perf_counter() - t0
+        n += 1
+        del d
+    return {"value": round(alg_total * n / busy / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} full passes of route+dispatch+combine over the {w.T}-token batch "
+                      f"({busy:.1f} s, single thread)",
+            "ms_per_step": round(busy / n * 1e3, 1), "host_cpus": os.cpu_count(),
+            "host_cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the routing path here runs on a single MI355X "
+              "(destination ranks are row ranges of one receive buffer); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from combine_moe_route_03_amd import _lib as moe
+    from combine_moe_route_03_amd.workloads import WORKLOADS, make_inputs
+    if not os.path.exists(moe.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        r = copy_ceiling(torch, 1.0, 5)
+        print(json.dumps({"calibration_copy": r}), flush=True)
+        return
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} N={w.N} "
+          f"payload={w.payload} out={w.out_dtype}; {args.sets} buffer sets", file=sys.stderr,
+          flush=True)
+    inp = make_inputs(w)
+    sets = [make_set(w, inp, dev, moe, torch) for _ in range(max(1, args.sets))]
+    phases = ("route", "layout", "pack", "combine")
+
+    def step(s):
+        for ph in phases:
+            s[ph]()
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+          for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        s, e = sets[i % len(sets)], ev[i]
+        e[0].record()
+        for p, ph in enumerate(phases):
+            s[ph]()
+            e[p + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / K
+    phase_us = {ph: sum(ev[i][p].elapsed_time(ev[i][p + 1]) for i in range(K)) / K * 1e3
+                for p, ph in enumerate(phases)}
+
+    alg = algorithmic_bytes(w)
+    alg_total = sum(alg.values())
+    value = alg_total / (ms_per_step * 1e-3) / 1e9
+    dominant = max(("pack", "combine"), key=lambda ph: phase_us[ph])
+    kernel_name = {"pack": "k_pack_copy" if w.payload != "fp8_e4m3" else "k_pack_fp8",
+                   "combine": "k_combine"}[dominant]
+    achieved = alg[dominant] / (phase_us[dominant] * 1e-6) / 1e9
+    ceiling = copy_ceiling(torch)
+    print(f"[bench] {ms_per_step * 1e3:.1f} us/step; phases " +
+          ", ".join(f"{ph} {phase_us[ph]:.1f} us" for ph in phases) +
+          f"; copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(w, args.cpu_seconds, alg_total)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.T} tokens, hidden {w.H} {w.x_dtype}, {w.E} experts "
+                               f"top-{w.k}, {w.N} ranks, {w.payload} payload, {w.out_dtype} out",
+                   "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "ranks": w.N,
+                   "payload": w.payload, "parallelism": "single GPU"},
+        "us_per_layer": round(ms_per_step * 1e3, 2),
+        "us_dispatch_plus_combine": round(phase_us["layout"] + phase_us["pack"] +
+                                          phase_us["combine"], 2),
+        "hbm_frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "phases_us": {ph: round(v, 2) for ph, v in phase_us.items()},
+        "algorithmic_bytes": alg,
+        "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": hbm_traffic(kernel_name),
+                     "algorithmic_bytes_per_launch": alg[dominant],
+                     "avg_launch_us": round(phase_us[dominant], 2)},
+        "copy_ceiling_GBps": round(ceiling["GBps"], 1),
+        "wall_s_timed_loop": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

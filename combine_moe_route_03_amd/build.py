@@ -8,6 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "moe_route.hip")
 LIB = os.path.join(PKG, "libmoe_route.so")
+BENCH_SRC = os.path.join(PKG, "csrc", "bench_copy.hip")
+BENCH_LIB = os.path.join(PKG, "libmoe_bench_copy.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -18,14 +20,20 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wal
          "-I", INCLUDE]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, SRC, "-o", tmp]
+def _compile(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the routing library and the benchmark's copy kernel; returns the library path."""
+    _compile(BENCH_SRC, BENCH_LIB, verbose)
+    return _compile(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -2,14 +2,16 @@
 """Benchmark of the MoE routing hot path on one MI355X.
 
 One step = the whole path over one batch already resident in HBM:
-  moe_route_topk -> moe_dispatch_layout -> moe_dispatch_pack -> moe_combine
+  moe_route_topk -> moe_dispatch -> moe_combine
 on the prefill batch (4096 tokens, hidden 7168 bf16, 384 experts, top-8, 48 destination ranks,
 bf16 payload and output). The expert outputs combine reads are emulated once before timing
 (row * (expert+1)/256), as the grouped GEMM is not part of the path.
 
 Prints ONE JSON line: value = algorithmic HBM bytes of a step / step time (GB/s), ms_per_step =
-µs per layer / 1000, per-kernel times from HIP events on the launch stream, the roofline of the
-dominant kernel, and the CPU oracle timed on the host.
+µs per layer / 1000, per-call times from HIP events on the launch stream, the roofline of the
+dominant kernel, and the CPU oracle timed on the host. A second timed loop runs the same step as
+route -> moe_dispatch_layout -> moe_dispatch_pack -> combine, so the packing kernel gets its own
+HIP-event timing.
 """
 from __future__ import annotations
 
@@ -102,6 +104,9 @@ def make_set(w, inp, dev, moe, torch):
                          P(buf.token_row.data_ptr()), code[w.payload], P(buf.recv.data_ptr()),
                          P(buf.recv_scales.data_ptr() if buf.recv_scales is not None else 0),
                          stream)
+    s["dispatch"] = Prepared(lib.moe_dispatch, P(x.data_ptr()), code[w.x_dtype], w.T, w.H,
+                             P(idx.data_ptr()), w.k, w.E, w.N, code[w.payload],
+                             ctypes.byref(struct), P(ws.data_ptr()), ws.numel(), stream)
     # one untimed pass, then the emulated expert outputs y = row * (expert+1)/256 (or identity)
     s["route"]()
     s["layout"]()
@@ -231,46 +236,61 @@ def main():
           flush=True)
     inp = make_inputs(w)
     sets = [make_set(w, inp, dev, moe, torch) for _ in range(max(1, args.sets))]
-    phases = ("route", "layout", "pack", "combine")
 
-    def step(s):
-        for ph in phases:
-            s[ph]()
+    def timed(phases, K, per_call_events):
+        """K steps of `phases` between two HIP events; with per_call_events, also an event after
+        every call (each costs a few us of GPU idle, so the headline loop records none).
+        Returns (ms per step, {phase: us} or None)."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+              for _ in range(K)] if per_call_events else None
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(K):
+            s = sets[i % len(sets)]
+            if ev is None:
+                for ph in phases:
+                    s[ph]()
+            else:
+                e = ev[i]
+                e[0].record()
+                for p, ph in enumerate(phases):
+                    s[ph]()
+                    e[p + 1].record()
+        end.record()
+        torch.cuda.synchronize()
+        per = None if ev is None else {
+            ph: sum(ev[i][p].elapsed_time(ev[i][p + 1]) for i in range(K)) / K * 1e3
+            for p, ph in enumerate(phases)}
+        return start.elapsed_time(end) / K, per
 
+    fused = ("route", "dispatch", "combine")
+    split = ("route", "layout", "pack", "combine")
     for i in range(args.warmup):
-        step(sets[i % len(sets)])
+        for ph in fused:
+            sets[i % len(sets)][ph]()
     torch.cuda.synchronize()
-
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
-          for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record()
-    for i in range(K):
-        s, e = sets[i % len(sets)], ev[i]
-        e[0].record()
-        for p, ph in enumerate(phases):
-            s[ph]()
-            e[p + 1].record()
-    end.record()
-    torch.cuda.synchronize()
+    ms_per_step, _ = timed(fused, K, False)          # the headline: no events inside the step
     wall = time.perf_counter() - wall0
-    ms_per_step = start.elapsed_time(end) / K
-    phase_us = {ph: sum(ev[i][p].elapsed_time(ev[i][p + 1]) for i in range(K)) / K * 1e3
-                for p, ph in enumerate(phases)}
+    ms_evented, phase_us = timed(fused, K, True)     # per-call times (events after every call)
+    ms_split, split_us = timed(split, K, True)       # packing kernel on its own
 
     alg = algorithmic_bytes(w)
     alg_total = sum(alg.values())
     value = alg_total / (ms_per_step * 1e-3) / 1e9
-    dominant = max(("pack", "combine"), key=lambda ph: phase_us[ph])
-    kernel_name = {"pack": "k_pack_copy" if w.payload != "fp8_e4m3" else "k_pack_fp8",
+    kernel_us = {"pack": split_us["pack"], "combine": phase_us["combine"]}
+    dominant = max(kernel_us, key=lambda ph: kernel_us[ph])
+    kernel_name = {"pack": "k_pack_rows" if w.payload != "fp8_e4m3" else "k_pack_rows_fp8",
                    "combine": "k_combine"}[dominant]
-    achieved = alg[dominant] / (phase_us[dominant] * 1e-6) / 1e9
+    achieved = alg[dominant] / (kernel_us[dominant] * 1e-6) / 1e9
     ceiling = copy_ceiling(torch)
-    print(f"[bench] {ms_per_step * 1e3:.1f} us/step; phases " +
-          ", ".join(f"{ph} {phase_us[ph]:.1f} us" for ph in phases) +
+    print(f"[bench] {ms_per_step * 1e3:.1f} us/step; with per-call events "
+          f"{ms_evented * 1e3:.1f} us/step: " +
+          ", ".join(f"{ph} {v:.1f} us" for ph, v in phase_us.items()) +
+          f" | split path {ms_split * 1e3:.1f} us/step: " +
+          ", ".join(f"{ph} {v:.1f} us" for ph, v in split_us.items()) +
           f"; copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
     cpu = None
@@ -297,17 +317,19 @@ def main():
                    "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "ranks": w.N,
                    "payload": w.payload, "parallelism": "single GPU"},
         "us_per_layer": round(ms_per_step * 1e3, 2),
-        "us_dispatch_plus_combine": round(phase_us["layout"] + phase_us["pack"] +
-                                          phase_us["combine"], 2),
+        "us_dispatch_plus_combine": round(phase_us["dispatch"] + phase_us["combine"], 2),
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "phases_us": {ph: round(v, 2) for ph, v in phase_us.items()},
+        "evented_ms_per_step": round(ms_evented, 5),
+        "split_path": {"ms_per_step": round(ms_split, 5),
+                       "phases_us": {ph: round(v, 2) for ph, v in split_us.items()}},
         "algorithmic_bytes": alg,
         "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": hbm_traffic(kernel_name),
                      "algorithmic_bytes_per_launch": alg[dominant],
-                     "avg_launch_us": round(phase_us[dominant], 2)},
+                     "avg_launch_us": round(kernel_us[dominant], 2)},
         "copy_ceiling_GBps": round(ceiling["GBps"], 1),
         "wall_s_timed_loop": round(wall, 4),
         "cpu_baseline": cpu,

@@ -73,8 +73,9 @@ moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k
 
 /*
  * Bytes of device workspace that moe_dispatch / moe_dispatch_layout need for (T, E, k): per-block
- * expert histograms and per-item ranks. Returns 0 for invalid sizes. The workspace needs no
- * initialisation and holds nothing the caller uses afterwards.
+ * expert histograms, their in-expert prefixes and per-item ranks. Returns 0 for invalid sizes.
+ * The workspace needs no initialisation and holds nothing the caller uses afterwards. Two calls
+ * that may run at the same time (different streams) must not share a workspace.
  */
 size_t moe_dispatch_workspace_bytes(int32_t T, int32_t E, int32_t k);
 

@@ -70,9 +70,10 @@ def test_workspace_bytes():
     assert ws(-1, 8, 2) == 0 and ws(4, 0, 2) == 0 and ws(4, 8, 0) == 0
     assert ws(2 ** 30, 8, 4) == 0
     assert ws(0, 8, 2) > 0
-    # histograms (<= 64 blocks x E u32) plus one u32 rank per row, 256-byte aligned pieces
+    # histogram and its scan (<= 64 blocks x E u32 each) plus one u32 rank per row, in
+    # 256-byte aligned pieces
     R = 4096 * 8
-    assert R * 4 <= ws(4096, 384, 8) <= R * 4 + 64 * 384 * 4 + 512
+    assert R * 4 <= ws(4096, 384, 8) <= R * 4 + 2 * (64 * 384 + 1) * 4 + 768
     assert ws(4096, 384, 8) % 256 == 0
     assert ws(128, 256, 8) >= 128 * 8 * 4
 

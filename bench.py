@@ -2,16 +2,16 @@
 """Benchmark of the MoE routing hot path on one MI355X.
 
 One step = the whole path over one batch already resident in HBM:
-  moe_route_topk -> moe_dispatch -> moe_combine
+  moe_route_dispatch (routing + dispatch in one call) -> moe_combine
 on the prefill batch (4096 tokens, hidden 7168 bf16, 384 experts, top-8, 48 destination ranks,
 bf16 payload and output). The expert outputs combine reads are emulated once before timing
 (row * (expert+1)/256), as the grouped GEMM is not part of the path.
 
 Prints ONE JSON line: value = algorithmic HBM bytes of a step / step time (GB/s), ms_per_step =
 µs per layer / 1000, per-call times from HIP events on the launch stream, the roofline of the
-dominant kernel, and the CPU oracle timed on the host. A second timed loop runs the same step as
-route -> moe_dispatch_layout -> moe_dispatch_pack -> combine, so the packing kernel gets its own
-HIP-event timing.
+dominant kernel, and the CPU oracle timed on the host. Two more timed loops run the same step as
+route -> moe_dispatch -> combine and as route -> moe_dispatch_layout -> moe_dispatch_pack ->
+combine, so the packing kernel gets its own HIP-event timing.
 """
 from __future__ import annotations
 
@@ -21,6 +21,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -107,6 +108,10 @@ def make_set(w, inp, dev, moe, torch):
     s["dispatch"] = Prepared(lib.moe_dispatch, P(x.data_ptr()), code[w.x_dtype], w.T, w.H,
                              P(idx.data_ptr()), w.k, w.E, w.N, code[w.payload],
                              ctypes.byref(struct), P(ws.data_ptr()), ws.numel(), stream)
+    s["route_dispatch"] = Prepared(lib.moe_route_dispatch, P(logits.data_ptr()), P(x.data_ptr()),
+                                   code[w.x_dtype], w.T, w.H, w.E, w.k, w.N, code[w.payload],
+                                   P(idx.data_ptr()), P(wt.data_ptr()), ctypes.byref(struct),
+                                   P(ws.data_ptr()), ws.numel(), stream)
     # one untimed pass, then the emulated expert outputs y = row * (expert+1)/256 (or identity)
     s["route"]()
     s["layout"]()
@@ -152,21 +157,23 @@ def copy_ceiling(torch, gib: float = 1.0, iters: int = 10):
     return {"bytes_per_launch": 2 * n, "us": ms * 1e3, "GBps": 2 * n / (ms * 1e-3) / 1e9}
 
 
-def hbm_traffic(kernel_key: str):
-    """Counter-measured HBM bytes per launch from the committed profile, or None when the
-    kernels changed since the counters were taken."""
+def hbm_traffic(kernel_pattern: str):
+    """Counter-measured HBM bytes per launch of the kernel whose name (template arguments
+    included) matches `kernel_pattern`, from the committed profile: (name, bytes), or
+    (None, None) when the kernels changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return None, None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
     with open(HIP_SRC, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec.get("source_sha256"):
-            return None
-    k = rec["kernels"].get(kernel_key)
-    if not k:
-        return None
-    return int(round(k["fetch_kib"] * 1024 * rec["copy_calibration"]["read_factor"] +
-                     k["write_kib"] * 1024 * rec["copy_calibration"]["write_factor"]))
+            return None, None
+    for name, k in rec["kernels"].items():
+        if re.fullmatch(kernel_pattern, name):
+            return name, int(round(k["fetch_kib"] * 1024 * rec["copy_calibration"]["read_factor"]
+                                   + k["write_kib"] * 1024 *
+                                   rec["copy_calibration"]["write_factor"]))
+    return None, None
 
 
 def cpu_baseline(w, seconds: float, alg_total: int):
@@ -264,31 +271,39 @@ def main():
             for p, ph in enumerate(phases)}
         return start.elapsed_time(end) / K, per
 
-    fused = ("route", "dispatch", "combine")
+    headline = ("route_dispatch", "combine")
+    separate = ("route", "dispatch", "combine")
     split = ("route", "layout", "pack", "combine")
     for i in range(args.warmup):
-        for ph in fused:
+        for ph in headline:
             sets[i % len(sets)][ph]()
     torch.cuda.synchronize()
     K = args.steps
     wall0 = time.perf_counter()
-    ms_per_step, _ = timed(fused, K, False)          # the headline: no events inside the step
+    ms_per_step, _ = timed(headline, K, False)       # the headline: no events inside the step
     wall = time.perf_counter() - wall0
-    ms_evented, phase_us = timed(fused, K, True)     # per-call times (events after every call)
+    ms_evented, phase_us = timed(headline, K, True)  # per-call times (events after every call)
+    ms_sep, sep_us = timed(separate, K, True)        # routing and dispatch as separate calls
     ms_split, split_us = timed(split, K, True)       # packing kernel on its own
 
     alg = algorithmic_bytes(w)
     alg_total = sum(alg.values())
     value = alg_total / (ms_per_step * 1e-3) / 1e9
+    # The dominant kernel: packing (the same kernel in every dispatch entry point, timed alone
+    # through moe_dispatch_pack) or combine.
     kernel_us = {"pack": split_us["pack"], "combine": phase_us["combine"]}
     dominant = max(kernel_us, key=lambda ph: kernel_us[ph])
-    kernel_name = {"pack": "k_pack_rows" if w.payload != "fp8_e4m3" else "k_pack_rows_fp8",
-                   "combine": "k_combine"}[dominant]
+    pattern = {"pack": r"k_pack_rows(_fp8<.*>)?", "combine": r"k_combine<.*>"}[dominant]
+    prof_name, traffic = hbm_traffic(pattern)
+    kernel_name = prof_name or {"pack": "k_pack_rows" if w.payload != "fp8_e4m3"
+                                else "k_pack_rows_fp8", "combine": "k_combine"}[dominant]
     achieved = alg[dominant] / (kernel_us[dominant] * 1e-6) / 1e9
     ceiling = copy_ceiling(torch)
     print(f"[bench] {ms_per_step * 1e3:.1f} us/step; with per-call events "
           f"{ms_evented * 1e3:.1f} us/step: " +
           ", ".join(f"{ph} {v:.1f} us" for ph, v in phase_us.items()) +
+          f" | separate calls {ms_sep * 1e3:.1f} us/step: " +
+          ", ".join(f"{ph} {v:.1f} us" for ph, v in sep_us.items()) +
           f" | split path {ms_split * 1e3:.1f} us/step: " +
           ", ".join(f"{ph} {v:.1f} us" for ph, v in split_us.items()) +
           f"; copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -317,17 +332,20 @@ def main():
                    "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "ranks": w.N,
                    "payload": w.payload, "parallelism": "single GPU"},
         "us_per_layer": round(ms_per_step * 1e3, 2),
-        "us_dispatch_plus_combine": round(phase_us["dispatch"] + phase_us["combine"], 2),
+        "us_route_dispatch_plus_combine": round(phase_us["route_dispatch"] +
+                                                phase_us["combine"], 2),
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "phases_us": {ph: round(v, 2) for ph, v in phase_us.items()},
         "evented_ms_per_step": round(ms_evented, 5),
+        "separate_calls": {"ms_per_step": round(ms_sep, 5),
+                           "phases_us": {ph: round(v, 2) for ph, v in sep_us.items()}},
         "split_path": {"ms_per_step": round(ms_split, 5),
                        "phases_us": {ph: round(v, 2) for ph, v in split_us.items()}},
         "algorithmic_bytes": alg,
         "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": hbm_traffic(kernel_name),
+                     "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg[dominant],
                      "avg_launch_us": round(kernel_us[dominant], 2)},
         "copy_ceiling_GBps": round(ceiling["GBps"], 1),

@@ -6,8 +6,9 @@ it has not been built.
 """
 
 _EXPORTS = ("moe_route_topk", "moe_dispatch_workspace_bytes", "moe_dispatch_layout",
-            "moe_dispatch_pack", "moe_dispatch", "moe_combine", "moe_status_str",
-            "alloc_dispatch_out", "alloc_workspace", "DispatchBuffers", "MoeError")
+            "moe_dispatch_pack", "moe_dispatch", "moe_route_dispatch", "moe_combine",
+            "moe_status_str", "alloc_dispatch_out", "alloc_workspace", "DispatchBuffers",
+            "MoeError")
 
 
 def __getattr__(name):

@@ -55,9 +55,10 @@ def load() -> ctypes.CDLL:
         lib.moe_dispatch_layout.argtypes = [P, I, I, I, I, P, P, Z, P]
         lib.moe_dispatch_pack.argtypes = [P, I, I, I, I, P, I, P, P, P]
         lib.moe_dispatch.argtypes = [P, I, I, I, P, I, I, I, I, P, P, Z, P]
+        lib.moe_route_dispatch.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, Z, P]
         lib.moe_combine.argtypes = [P, I, I, I, I, P, P, P, I, P]
         for fn in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_dispatch",
-                   "moe_combine"):
+                   "moe_route_dispatch", "moe_combine"):
             getattr(lib, fn).restype = I
         _lib = lib
     return _lib
@@ -179,6 +180,26 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, n_ranks: int,
         _dtype_code(out.recv, fp8_ok=True), ctypes.byref(st), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, n_ranks: int,
+                       out: DispatchBuffers, workspace: torch.Tensor,
+                       topk_idx: Optional[torch.Tensor] = None,
+                       topk_w: Optional[torch.Tensor] = None, stream=None):
+    """Route (top-k ids and weights) and dispatch in one call; returns (topk_idx, topk_w, out)."""
+    T, E = logits.shape
+    H = x.shape[1]
+    assert logits.dtype == torch.float32 and logits.is_contiguous() and x.shape[0] == T
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    st = out.as_struct()
+    _check("moe_route_dispatch", load().moe_route_dispatch(
+        _ptr(logits), _ptr(x), _dtype_code(x), T, H, E, k, n_ranks,
+        _dtype_code(out.recv, fp8_ok=True), _ptr(topk_idx), _ptr(topk_w), ctypes.byref(st),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return topk_idx, topk_w, out
 
 
 def moe_combine(y: torch.Tensor, token_row: torch.Tensor, topk_w: torch.Tensor,

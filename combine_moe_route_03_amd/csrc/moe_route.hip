@@ -8,17 +8,20 @@
 //
 // The path moves bytes; it has no dense contraction, so it uses no MFMA. Every kernel is bound by
 // HBM bandwidth or by latency:
-//   k_route_topk     one wavefront per token, k rounds of a wave-wide 64-bit max built from DPP
-//                    row operations and four readlanes;
-//   k_layout_hist    per block of items: stable in-block ranks from LDS bit masks, and the
-//                    block's expert histogram, stored expert-major;
-//   k_layout_scan    one workgroup: per expert, a DPP wave scan over the blocks' counts gives
-//                    the rows of that expert in earlier blocks; a block scan over the expert
-//                    totals gives the expert offsets;
-//   k_layout_rows    token_row / row_token from the scan, the in-block ranks and the ids;
-//   k_pack_rows      one wavefront per (token, slot, part of the row): reads the x row (from the
-//                    XCD's L2 after the first of the token's wavefronts) and writes one whole
-//                    contiguous row with 16-byte non-temporal stores;
+//   k_route_topk     one wavefront per token: the lane-sorted candidates give up their heads over
+//                    k rounds of a wave-wide max (DPP row operations and four readlanes);
+//   k_route_layout   the same routing, 16 tokens per workgroup, and in the same launch the
+//                    workgroup's expert histogram and the stable in-workgroup rank of every
+//                    (token, slot) from one LDS bit mask per expert;
+//   k_layout_hist    for caller-given expert ids: per block of items, stable in-block ranks from
+//                    per-wavefront LDS bit masks, and the block's expert histogram;
+//   k_expert_scan    one wavefront per expert scans its blocks' counts into per-block prefixes
+//                    and the expert's total (many workgroups);
+//   k_layout_rows    every workgroup scans the expert totals into offsets in LDS, then writes
+//                    token_row / row_token; workgroup 0 writes the counts and offsets;
+//   k_pack_rows      one wavefront per (token, slot, 1 KB piece of the row): a 16-byte load of
+//                    x (from the XCD's L2 after the first of the token's wavefronts) and a
+//                    16-byte non-temporal store per lane; the pieces of a row run side by side;
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
 //                    fp32 fused multiply-adds, one 16-byte store per 8 outputs.
@@ -30,14 +33,15 @@
 
 namespace {
 
-constexpr int kThreads = 256;            // route / layout workgroups: 4 wavefronts
+constexpr int kThreads = 256;            // route / histogram workgroups: 4 wavefronts
 constexpr int kWaves = kThreads / 64;
-constexpr int kScanThreads = 1024;       // the single scan workgroup: 16 wavefronts
-constexpr int kMaxLayoutBlocks = 64;     // histogram blocks: one per lane of a scan wavefront
-constexpr int kPackWaves = 2;            // wavefronts per pack workgroup
+constexpr int kGroupThreads = 1024;      // 16-wavefront workgroups (route-layout, totals, scan)
+constexpr int kGroupWaves = kGroupThreads / 64;
+constexpr int kRouteTokens = kGroupWaves;   // tokens per route-layout workgroup (one per wave)
+constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
+constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
 constexpr int kCombineWaves = 2;         // wavefronts per combine workgroup
 constexpr int kXcds = 8;                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
-constexpr int64_t kTargetWaves = 16384;  // wavefronts the row kernels aim for (64 per CU)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -166,23 +170,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return max(max(a, b), max(c, d));
 }
 
-// One wavefront per token. Lane l holds experts l, l+64, ... (coalesced loads) and sorts its
-// keys once, largest first, so its best remaining candidate is always key[0]. Each of the k
-// rounds takes the wave-wide maximum of the candidates' logit words; when a single lane holds it
-// (the usual case, found with one ballot) that lane wins, otherwise the lowest expert id among
-// the tied lanes wins. The winner drops its head. The weights use double-precision exp and
-// division, rounded once to fp32.
+// Top-k of one token by one whole wavefront (all lanes active). Lane l holds experts l, l+64, ...
+// (coalesced loads) and sorts its keys once, largest first, so its best remaining candidate is
+// always key[0]. Each of the k rounds takes the wave-wide maximum of the candidates' logit words;
+// when a single lane holds it (the usual case, found with one ballot) that lane wins, otherwise the
+// lowest expert id among the tied lanes wins. The winner drops its head. The weights use
+// double-precision exp and division, rounded once to fp32. Lane j < k writes slot j and returns
+// its expert id (other lanes return -1).
 template <int PL>
-__global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict__ logits,
-                                                         int32_t T, int32_t E, int32_t k,
-                                                         int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_w)
+__device__ __forceinline__ int route_token(const float* __restrict__ l, int32_t E, int32_t k,
+                                           int32_t* __restrict__ idx_out,
+                                           float* __restrict__ w_out)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (t >= T)
-        return;                                          // uniform: whole wavefronts leave
-    const float* l = logits + t * E;
     uint64_t key[PL];
 #pragma unroll
     for (int p = 0; p < PL; ++p) {
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict
                 key[p] = key[p + 1];
                 key[p + 1] = tmp;
             }
-    int my_id = 0;
+    int my_id = -1;
     float my_logit = 0.0f, top_logit = 0.0f;
     for (int j = 0; j < k; ++j) {
         const uint32_t hi = (uint32_t)(key[0] >> 32);
@@ -229,44 +229,89 @@ __global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict
     const double ex = (lane < k) ? exp((double)my_logit - (double)top_logit) : 0.0;
     const double sum = wave_sum_f64(ex);
     if (lane < k) {
-        topk_idx[t * k + lane] = my_id;
-        topk_w[t * k + lane] = (float)(ex / sum);
+        idx_out[lane] = my_id;
+        w_out[lane] = (float)(ex / sum);
     }
+    return my_id;
+}
+
+template <int PL>
+__global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict__ logits,
+                                                         int32_t T, int32_t E, int32_t k,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w)
+{
+    const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (t >= T)
+        return;                                          // uniform: whole wavefronts leave
+    route_token<PL>(logits + t * E, E, k, topk_idx + t * k, topk_w + t * k);
+}
+
+// Routing plus the counting half of dispatch in one launch. Workgroup b routes tokens
+// 16b .. 16b+15 (wavefront w takes token 16b + w); each selected (token, slot) sets bit w of
+// the LDS mask of its expert. A token's k experts are distinct, so the rank of (token, slot)
+// among the workgroup's items of the same expert, in (token, slot) order, is the number of bits
+// below w, and the workgroup's count of expert e is popcount(mask[e]), stored expert-major at
+// hist_t[e * nblk + b]. LDS: mask [E] u32.
+template <int PL>
+__global__ __launch_bounds__(kGroupThreads) void k_route_layout(
+    const float* __restrict__ logits, int32_t T, int32_t E, int32_t k, int32_t nblk,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ hist_t,
+    uint32_t* __restrict__ local_rank)
+{
+    extern __shared__ uint32_t lds_mask[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += kGroupThreads)
+        lds_mask[e] = 0u;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kRouteTokens + wave;
+    const bool active = t < T;                          // uniform per wavefront
+    int my_id = -1;
+    if (active)
+        my_id = route_token<PL>(logits + t * E, E, k, topk_idx + t * k, topk_w + t * k);
+    if (my_id >= 0)
+        atomicOr(&lds_mask[my_id], 1u << wave);
+    __syncthreads();
+    if (my_id >= 0)
+        local_rank[t * k + lane] = (uint32_t)__popc(lds_mask[my_id] & ((1u << wave) - 1u));
+    for (int e = tid; e < E; e += kGroupThreads)
+        hist_t[(int64_t)e * nblk + blockIdx.x] = (uint32_t)__popc(lds_mask[e]);
 }
 
 // --------------------------------------------------------------------------------- layout --
-// Items are the (token, slot) pairs in index order i = t*k + j. Block b owns the contiguous items
-// [b*rows_per_block, (b+1)*rows_per_block) and walks them 64*W at a time (W wavefronts). For
-// each group, every item sets its lane bit in the LDS mask of (its wavefront, its expert); its
-// rank among the block's items of the same expert is then
+// Items are the (token, slot) pairs in index order i = t*k + j.
+//
+// Caller-given ids (which may repeat within a token): block b owns the contiguous items
+// [b*rows_per_block, (b+1)*rows_per_block) and walks them 256 at a time. For each group, every
+// item sets its lane bit in the LDS mask of (its wavefront, its expert); its rank among the
+// block's items of the same expert is then
 //   run[e] + (bits of e in lower wavefronts) + (bits of e in lower lanes of its own wavefront),
 // which keeps index order without any atomic deciding a position. The first item of each expert
 // in the group then advances run[e] and clears the masks. The block's counts go to
-// hist_t[e * nblk + b] (expert-major). LDS: masks [W][E] u64, run [E] u32.
-template <int W>
-__device__ __forceinline__ void block_histogram(const int32_t* __restrict__ topk_idx, int32_t R,
-                                                int32_t E, int32_t rows_per_block, int32_t nblk,
-                                                uint32_t* __restrict__ hist_t,
-                                                uint32_t* __restrict__ local_rank,
-                                                uint64_t* lds)
+// hist_t[e * nblk + b] (expert-major). LDS: masks [4][E] u64, run [E] u32.
+__global__ __launch_bounds__(kThreads) void k_layout_hist(const int32_t* __restrict__ topk_idx,
+                                                          int32_t R, int32_t E,
+                                                          int32_t rows_per_block, int32_t nblk,
+                                                          uint32_t* __restrict__ hist_t,
+                                                          uint32_t* __restrict__ local_rank)
 {
-    constexpr int NT = 64 * W;
-    uint64_t* mask = lds;
-    uint32_t* run = reinterpret_cast<uint32_t*>(mask + W * E);
+    extern __shared__ uint64_t lds_u64[];
+    uint64_t* mask = lds_u64;
+    uint32_t* run = reinterpret_cast<uint32_t*>(mask + kWaves * E);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < W * E; i += NT)
+    for (int i = tid; i < kWaves * E; i += kThreads)
         mask[i] = 0ull;
-    for (int i = tid; i < E; i += NT)
+    for (int i = tid; i < E; i += kThreads)
         run[i] = 0u;
     const uint64_t lower_lanes = (1ull << lane) - 1ull;
     const int64_t first = (int64_t)blockIdx.x * rows_per_block;
     const int64_t last = first + rows_per_block < R ? first + rows_per_block : R;
     int e_next = (first + tid < last) ? topk_idx[first + tid] : -1;
     __syncthreads();
-    for (int64_t i = first + tid; i - tid < last; i += NT) {
+    for (int64_t i = first + tid; i - tid < last; i += kThreads) {
         int e = e_next;
-        if (i + NT < last)
-            e_next = topk_idx[i + NT];                  // prefetch the next group's id
+        if (i + kThreads < last)
+            e_next = topk_idx[i + kThreads];            // prefetch the next group's id
         if (i >= last || (uint32_t)e >= (uint32_t)E)
             e = -1;                                      // past the range, or an id outside [0, E)
         if (e >= 0)
@@ -285,7 +330,7 @@ __device__ __forceinline__ void block_histogram(const int32_t* __restrict__ topk
         __syncthreads();
         if (leader) {
             uint32_t n = 0u;
-            for (int w = 0; w < W; ++w) {
+            for (int w = 0; w < kWaves; ++w) {
                 n += (uint32_t)__popcll(mask[w * E + e]);
                 mask[w * E + e] = 0ull;
             }
@@ -295,14 +340,14 @@ __device__ __forceinline__ void block_histogram(const int32_t* __restrict__ topk
         if (i < last)
             local_rank[i] = rank;
     }
-    for (int e = tid; e < E; e += NT)
+    for (int e = tid; e < E; e += kThreads)
         hist_t[(int64_t)e * nblk + blockIdx.x] = run[e];
 }
 
 // Exclusive scan of one value per thread over the NT threads of the block; returns the prefix
-// and writes the block total to *total. `scratch` holds NT/64 words of LDS.
+// and writes the block total to *total. `wave_tot` holds NT/64 words of LDS.
 template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
                                                          uint32_t* total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -314,12 +359,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
             x += y;
     }
     if (lane == 63)
-        scratch[wave] = x;
+        wave_tot[wave] = x;
     __syncthreads();
     uint32_t base = 0u, all = 0u;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
-        const uint32_t s = scratch[w];
+        const uint32_t s = wave_tot[w];
         base += (w < wave) ? s : 0u;
         all += s;
     }
@@ -341,120 +386,115 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v)
     return v;
 }
 
-// Offsets from the expert-major histograms, by one workgroup of 16 wavefronts. Wavefront w
-// takes experts w, w+16, ...; for expert e, lane b holds hist_t[e * nblk + b] (nblk <= 64) and a
-// wave scan gives prefix[e * nblk + b] = rows of e in blocks before b (stored at once, so the
-// stores drain during the rest); the last lane gives e's total. A block scan over the E totals
-// gives the expert offsets; the row of item i of block b with expert e is then
-// expert_offsets[e] + prefix[e * nblk + b] + local_rank[i]. Also writes the rank counts and
-// offsets. EPW >= ceil(E / 16).
-template <int EPW>
-__device__ __forceinline__ void scan_histograms(const uint32_t* __restrict__ hist_t, int32_t E,
-                                                int32_t N, int32_t nblk,
-                                                uint32_t* __restrict__ prefix,
-                                                int32_t* __restrict__ expert_counts,
-                                                int32_t* __restrict__ expert_offsets,
-                                                int32_t* __restrict__ rank_counts,
-                                                int32_t* __restrict__ rank_offsets,
-                                                uint32_t* scratch, uint32_t* eoff)
+// Scan of the block histograms, one wavefront per expert e (16 per workgroup, many workgroups).
+// Lane l holds the counts of blocks l*S .. l*S+S-1 of e's expert-major row; a wave scan of the
+// lane sums gives prefix[e * nblk + b] = rows of e in blocks before b, and e's total goes to
+// totals[e]. Requires nblk <= 64 * S (nblk = 0 gives zero totals).
+template <int S>
+__global__ __launch_bounds__(kGroupThreads) void k_expert_scan(const uint32_t* __restrict__ hist_t,
+                                                               int32_t E, int32_t nblk,
+                                                               uint32_t* __restrict__ prefix,
+                                                               uint32_t* __restrict__ totals)
 {
-    constexpr int kWavesS = kScanThreads / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t cnt[EPW];
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * kGroupWaves + (threadIdx.x >> 6);
+    if (e >= E)
+        return;                                          // uniform per wavefront
+    uint32_t c[S];
+    uint32_t sum = 0u;
 #pragma unroll
-    for (int u = 0; u < EPW; ++u) {
-        const int e = wave + kWavesS * u;
-        cnt[u] = (e < E && lane < nblk) ? hist_t[(int64_t)e * nblk + lane] : 0u;
+    for (int s = 0; s < S; ++s) {
+        const int b = lane * S + s;
+        c[s] = b < nblk ? hist_t[(int64_t)e * nblk + b] : 0u;
+        sum += c[s];
     }
+    const uint32_t incl = wave_inclusive_scan_u32(sum);
+    uint32_t run = incl - sum;
 #pragma unroll
-    for (int u = 0; u < EPW; ++u) {
-        const int e = wave + kWavesS * u;
-        if (e < E) {                                    // uniform per wavefront
-            const uint32_t incl = wave_inclusive_scan_u32(cnt[u]);
-            if (lane < nblk)
-                prefix[(int64_t)e * nblk + lane] = incl - cnt[u];
-            if (lane == 63)
-                eoff[e] = incl;                         // expert total, for now
-        }
+    for (int s = 0; s < S; ++s) {
+        const int b = lane * S + s;
+        if (b < nblk)
+            prefix[(int64_t)e * nblk + b] = run;
+        run += c[s];
     }
-    __syncthreads();
-    const uint32_t mine = tid < E ? eoff[tid] : 0u;     // E <= 1024: one expert per thread
-    uint32_t total = 0u;
-    const uint32_t ex = block_exclusive_scan<kScanThreads>(mine, scratch, &total);
-    __syncthreads();                                    // every total read before overwriting
-    if (tid < E)
-        eoff[tid] = ex;
-    if (tid == 0)
-        eoff[E] = total;
-    __syncthreads();
-    const int epr = E / N;
-    for (int i = tid; i < E; i += kScanThreads) {
-        expert_offsets[i] = (int32_t)eoff[i];
-        expert_counts[i] = (int32_t)(eoff[i + 1] - eoff[i]);
-    }
-    for (int r = tid; r < N; r += kScanThreads) {
-        rank_offsets[r] = (int32_t)eoff[r * epr];
-        rank_counts[r] = (int32_t)(eoff[(r + 1) * epr] - eoff[r * epr]);
-    }
-    if (tid == 0) {
-        expert_offsets[E] = (int32_t)total;
-        rank_offsets[N] = (int32_t)total;
-    }
+    if (lane == 63)
+        totals[e] = incl;
 }
 
-// Histogram blocks of 4 wavefronts (256 items per pass).
-__global__ __launch_bounds__(kThreads) void k_layout_hist(const int32_t* __restrict__ topk_idx,
-                                                          int32_t R, int32_t E,
-                                                          int32_t rows_per_block, int32_t nblk,
-                                                          uint32_t* __restrict__ hist_t,
-                                                          uint32_t* __restrict__ local_rank)
-{
-    extern __shared__ uint64_t lds_u64[];
-    block_histogram<kWaves>(topk_idx, R, E, rows_per_block, nblk, hist_t, local_rank, lds_u64);
-}
+// The count outputs of dispatch: expert and rank counts and offsets (offsets end with the row
+// count at [E] / [N]); rank r hosts experts [r*E/N, (r+1)*E/N).
+struct CountOutputs {
+    int32_t* expert_counts;
+    int32_t* expert_offsets;
+    int32_t* rank_counts;
+    int32_t* rank_offsets;
+    int32_t N;
+};
 
-// The scan as its own launch of one workgroup; with T = 0 it alone runs and writes zero counts.
-template <int EPW>
-__global__ __launch_bounds__(kScanThreads) void k_layout_scan(
-    const uint32_t* __restrict__ hist_t, int32_t E, int32_t N, int32_t nblk,
-    uint32_t* __restrict__ prefix, int32_t* __restrict__ expert_counts,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
-    int32_t* __restrict__ rank_offsets)
-{
-    __shared__ uint32_t scratch[kScanThreads / 64];
-    __shared__ uint32_t eoff[MOE_MAX_EXPERTS + 1];
-    scan_histograms<EPW>(hist_t, E, N, nblk, prefix, expert_counts, expert_offsets, rank_counts,
-                         rank_offsets, scratch, eoff);
-}
-
-// Everything a kernel needs to place item i = t*k + j: either the finished token_row, or the
-// layout results from which the row is computed (and token_row / row_token written).
 struct RowPlan {
     const int32_t* topk_idx;
     const uint32_t* local_rank;
     const uint32_t* prefix;
-    const int32_t* expert_offsets;
+    const uint32_t* totals;
     int32_t* token_row;
     int32_t* row_token;
     int32_t E, nblk, rows_per_block;
 };
 
-// Row of item i from the layout results, or -1 for an expert id outside [0, E).
-__device__ __forceinline__ int32_t planned_row(const RowPlan& rp, int64_t i)
+// Rows of the items. Every workgroup first turns the E expert totals into expert offsets (an
+// exclusive scan in LDS: E <= 1024 is four values a thread); workgroup 0 also writes the count
+// outputs. Item i of block b with expert e then takes row
+// expert_offset[e] + prefix[e * nblk + b] + local_rank[i], recorded in token_row[i] and
+// row_token[row]; an id outside [0, E) gets token_row -1 and no row. LDS: eoff [E + 1] u32.
+__global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R, int32_t k,
+                                                          CountOutputs co)
 {
-    const int e = rp.topk_idx[i];
-    if ((uint32_t)e >= (uint32_t)rp.E)
-        return -1;
-    const int64_t b = i / rp.rows_per_block;
-    return (int32_t)((uint32_t)rp.expert_offsets[e] + rp.prefix[(int64_t)e * rp.nblk + b] +
-                     rp.local_rank[i]);
-}
-
-__global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R, int32_t k)
-{
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < R;
+    constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
+    __shared__ uint32_t eoff[MOE_MAX_EXPERTS + 1];
+    __shared__ uint32_t wave_tot[kWaves];
+    const int tid = threadIdx.x, E = rp.E;
+    uint32_t v[kPer];
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int e = tid * kPer + u;
+        v[u] = e < E ? rp.totals[e] : 0u;
+        mine += v[u];
+    }
+    uint32_t total = 0u;
+    uint32_t run = block_exclusive_scan<kThreads>(mine, wave_tot, &total);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int e = tid * kPer + u;
+        if (e < E)
+            eoff[e] = run;
+        run += v[u];
+    }
+    if (tid == 0)
+        eoff[E] = total;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        const int epr = E / co.N;
+        for (int e = tid; e < E; e += kThreads) {
+            co.expert_offsets[e] = (int32_t)eoff[e];
+            co.expert_counts[e] = (int32_t)(eoff[e + 1] - eoff[e]);
+        }
+        for (int r = tid; r < co.N; r += kThreads) {
+            co.rank_offsets[r] = (int32_t)eoff[r * epr];
+            co.rank_counts[r] = (int32_t)(eoff[(r + 1) * epr] - eoff[r * epr]);
+        }
+        if (tid == 0) {
+            co.expert_offsets[E] = (int32_t)total;
+            co.rank_offsets[co.N] = (int32_t)total;
+        }
+    }
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < R;
          i += (int64_t)gridDim.x * kThreads) {
-        const int32_t row = planned_row(rp, i);
+        const int e = rp.topk_idx[i];
+        int32_t row = -1;
+        if ((uint32_t)e < (uint32_t)E)
+            row = (int32_t)(eoff[e] + rp.prefix[(int64_t)e * rp.nblk + i / rp.rows_per_block] +
+                            rp.local_rank[i]);
         rp.token_row[i] = row;
         if ((uint32_t)row < (uint32_t)R)
             rp.row_token[row] = (int32_t)(i / k);
@@ -481,76 +521,30 @@ __device__ __forceinline__ XcdItem xcd_item(int waves_per_group, int items_per_t
     return it;
 }
 
-// Row of (token t, slot j): from token_row, or planned (the part-0 wavefront then records it).
-template <bool PLANNED>
-__device__ __forceinline__ int32_t pack_row(const RowPlan& rp, int64_t t, int j, int k, int part,
-                                            int32_t R)
-{
-    const int64_t i = t * k + j;
-    int32_t row;
-    if constexpr (PLANNED) {
-        row = planned_row(rp, i);
-        if (part == 0 && (threadIdx.x & 63) == 0) {
-            rp.token_row[i] = row;
-            if ((uint32_t)row < (uint32_t)R)
-                rp.row_token[row] = (int32_t)t;
-        }
-    } else {
-        row = rp.token_row[i];
-    }
-    return row;
-}
-
-// One wavefront per (token, slot, part): chunks [part*cpp, (part+1)*cpp) (16 bytes each) of x's
-// row t are loaded (plain loads: the k wavefronts of the token share them through L2) and
-// stored to row token_row[t*k+j] with non-temporal stores, U chunks per lane at a time. The
-// first loads are issued before the row is known.
-template <int U, bool PLANNED>
+// One wavefront per (token t, slot j, piece of 64 chunks): lane l copies chunk piece*64 + l
+// (16 bytes) of x's row t to row token_row[t*k + j] with a non-temporal store. The x load (plain:
+// the k*pieces wavefronts of the token share the row through the XCD's L2) is issued before the
+// row is read. Pieces of one row sit in consecutive wavefronts, so a whole row is written at
+// nearly the same time. A row outside [0, R) is skipped.
 __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows(const u32x4* __restrict__ x,
                                                                int32_t T, int32_t k, int32_t R,
                                                                int32_t chunks_per_row,
-                                                               int32_t parts,
-                                                               int32_t chunks_per_part,
-                                                               RowPlan rp,
+                                                               int32_t pieces,
+                                                               const int32_t* __restrict__ token_row,
                                                                u32x4* __restrict__ recv)
 {
-    const XcdItem it = xcd_item(kPackWaves, k * parts);
+    const XcdItem it = xcd_item(kPackWaves, k * pieces);
     if (it.token >= T)
         return;
-    const int j = it.sub / parts, part = it.sub - j * parts;
-    const int lane = threadIdx.x & 63;
-    const int c0 = part * chunks_per_part;
-    const int c1 = min(chunks_per_row, c0 + chunks_per_part);
-    const u32x4* src = x + it.token * chunks_per_row;
-    u32x4 v[U];
-    int cb = c0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = cb + u * 64 + lane;
-        if (c < c1)
-            v[u] = src[c];
-    }
-    const int32_t row = pack_row<PLANNED>(rp, it.token, j, k, part, R);
-    if ((uint32_t)row >= (uint32_t)R)
-        return;
-    u32x4* dst = recv + (int64_t)row * chunks_per_row;
-    while (true) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = cb + u * 64 + lane;
-            if (c < c1)
-                __builtin_nontemporal_store(v[u], dst + c);
-        }
-        cb += 64 * U;
-        if (cb >= c1)
-            break;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = cb + u * 64 + lane;
-            if (c < c1)
-                v[u] = src[c];
-        }
-    }
+    const int j = it.sub / pieces, piece = it.sub - j * pieces;
+    const int c = piece * 64 + (threadIdx.x & 63);
+    const bool active = c < chunks_per_row;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (active)
+        v = x[it.token * chunks_per_row + c];
+    const int32_t row = token_row[it.token * k + j];
+    if (active && (uint32_t)row < (uint32_t)R)
+        __builtin_nontemporal_store(v, recv + (int64_t)row * chunks_per_row + c);
 }
 
 // Eight consecutive elements of x as fp32.
@@ -584,64 +578,51 @@ struct Load8<uint16_t> {
     }
 };
 
-// fp8 packing, one wavefront per (token, slot, part). A chunk is 8 elements; the 16 lanes of a
-// DPP row hold the 128 elements of one scale block (parts are multiples of 16 chunks, so rows
-// never straddle two blocks). Every lane stays active through the reduction; only stores are
-// masked. The row is resolved after the first chunk group has been loaded and quantised.
-template <typename XT, bool PLANNED>
+// fp8 packing, one wavefront per (token t, slot j, piece of 64 chunks of 8 elements). The 16
+// lanes of a DPP row hold the 128 elements of one scale block (H % 128 == 0, so a row of lanes is
+// all active or all inactive); every lane takes part in the reduction, only the stores are
+// masked. Scale s = amax / 448 (1 for an all-zero block), codes e4m3(x / s). The row is read
+// after the block has been quantised.
+template <typename XT>
 __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
-    const XT* __restrict__ x, int32_t T, int32_t H, int32_t k, int32_t R, int32_t parts,
-    int32_t chunks_per_part, RowPlan rp, uint8_t* __restrict__ recv,
+    const XT* __restrict__ x, int32_t T, int32_t H, int32_t k, int32_t R, int32_t pieces,
+    const int32_t* __restrict__ token_row, uint8_t* __restrict__ recv,
     float* __restrict__ recv_scales)
 {
-    const XcdItem it = xcd_item(kPackWaves, k * parts);
+    const XcdItem it = xcd_item(kPackWaves, k * pieces);
     if (it.token >= T)
         return;
-    const int j = it.sub / parts, part = it.sub - j * parts;
+    const int j = it.sub / pieces, piece = it.sub - j * pieces;
     const int lane = threadIdx.x & 63;
-    const int chunks_per_row = H / 8;
-    const int nb = H / 128;
-    const int c0 = part * chunks_per_part;
-    const int c1 = min(chunks_per_row, c0 + chunks_per_part);
-    const XT* src = x + it.token * H;
-    int32_t row = -1;
-    uint8_t* dst = nullptr;
-    for (int cb = c0; cb < c1; cb += 64) {
-        const int c = cb + lane;
-        const bool active = c < c1;
-        float v[8];
-        if (active) {
-            Load8<XT>::run(src + (int64_t)c * 8, v);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = 0.0f;
-        }
-        float amax = 0.0f;
+    const int c = piece * 64 + lane;
+    const bool active = c < H / 8;
+    float v[8];
+    if (active) {
+        Load8<XT>::run(x + it.token * H + (int64_t)c * 8, v);
+    } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            amax = fmaxf(amax, fabsf(v[i]));
-        amax = max_row16_f32(amax);
-        const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;   // correctly rounded division
-        uint32_t q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            q[i] = f32_to_e4m3(v[i] / s);
-        u32x2 packed;
-        packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-        if (cb == c0) {
-            row = pack_row<PLANNED>(rp, it.token, j, k, part, R);
-            if ((uint32_t)row >= (uint32_t)R)
-                return;
-            dst = recv + (int64_t)row * H;
-        }
-        if (active) {
-            __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(dst) + c);
-            if ((lane & 15) == 0)
-                recv_scales[(int64_t)row * nb + c / 16] = s;
-        }
+            v[i] = 0.0f;
     }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        amax = fmaxf(amax, fabsf(v[i]));
+    amax = max_row16_f32(amax);
+    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;   // correctly rounded division
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        q[i] = f32_to_e4m3(v[i] / s);
+    u32x2 packed;
+    packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+    packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+    const int32_t row = token_row[it.token * k + j];
+    if (!active || (uint32_t)row >= (uint32_t)R)
+        return;
+    __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(recv + (int64_t)row * H) + c);
+    if ((lane & 15) == 0)
+        recv_scales[(int64_t)row * (H / 128) + c / 16] = s;
 }
 
 // ----------------------------------------------------------------------------------- combine --
@@ -777,83 +758,82 @@ inline bool is_wide(moe_dtype_t d) { return d == MOE_F32 || d == MOE_BF16; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Layout launch plan: histogram blocks of 4 wavefronts walk their items 256 at a time; at most
-// 64 blocks (one lane each in the scan).
+// Layout blocks. Caller-given ids: blocks of 4 wavefronts walk their items 256 at a time, at
+// most kMaxScanBlocks blocks. Fused routing: one block per 16 tokens (T <= 16 * kMaxScanBlocks).
 struct LayoutPlan {
     int32_t rows_per_block;
     int32_t nblk;
 };
+
+inline LayoutPlan hist_plan(int64_t R)
+{
+    LayoutPlan p;
+    const int64_t groups = R > 0 ? ceil_div(R, (int64_t)kThreads * kMaxScanBlocks) : 1;
+    p.rows_per_block = (int32_t)(groups * kThreads);
+    p.nblk = (int32_t)ceil_div(R, p.rows_per_block);
+    return p;
+}
+
+inline bool fused_route_fits(int32_t T) { return T <= kMaxScanBlocks * kRouteTokens; }
+
+inline LayoutPlan route_plan(int32_t T, int32_t k)
+{
+    LayoutPlan p;
+    p.rows_per_block = kRouteTokens * k;
+    p.nblk = (int32_t)ceil_div(T, kRouteTokens);
+    return p;
+}
 
 inline size_t hist_lds_bytes(int32_t E)
 {
     return (size_t)kWaves * E * sizeof(uint64_t) + (size_t)E * sizeof(uint32_t);
 }
 
-inline LayoutPlan layout_plan(int64_t R)
-{
-    LayoutPlan p;
-    const int64_t groups = R > 0 ? ceil_div(R, (int64_t)kThreads * kMaxLayoutBlocks) : 1;
-    p.rows_per_block = (int32_t)(groups * kThreads);
-    p.nblk = (int32_t)ceil_div(R, p.rows_per_block);
-    return p;
-}
-
-// Workspace: expert-major histograms [E * nblk], in-expert prefixes [E * nblk], in-block ranks
-// [R]; each piece 256-byte aligned.
+// Workspace: expert-major histograms [E * nblk], per-block prefixes [E * nblk], expert totals
+// [E], in-block ranks [R]; each piece 256-byte aligned; nblk covers both layout plans.
 struct Workspace {
     uint32_t* hist_t;
     uint32_t* prefix;
+    uint32_t* totals;
     uint32_t* local_rank;
 };
 
-inline size_t ws_hist_bytes(int64_t R, int32_t E)
+inline int64_t ws_nblk(int32_t T, int32_t k)
 {
-    return align_up(((size_t)layout_plan(R).nblk * E + 1) * sizeof(uint32_t), 256);
+    int64_t n = hist_plan((int64_t)T * k).nblk;
+    if (fused_route_fits(T) && route_plan(T, k).nblk > n)
+        n = route_plan(T, k).nblk;
+    return n;
 }
 
-inline size_t ws_bytes(int64_t R, int32_t E)
+inline size_t ws_hist_bytes(int32_t T, int32_t E, int32_t k)
 {
-    return 2 * ws_hist_bytes(R, E) + align_up((size_t)(R > 0 ? R : 1) * 4, 256);
+    return align_up(((size_t)ws_nblk(T, k) * E + 1) * sizeof(uint32_t), 256);
 }
 
-inline Workspace carve_workspace(void* base, int64_t R, int32_t E)
+inline size_t ws_bytes(int32_t T, int32_t E, int32_t k)
+{
+    const int64_t R = (int64_t)T * k;
+    return 2 * ws_hist_bytes(T, E, k) + align_up((size_t)E * sizeof(uint32_t), 256) +
+           align_up((size_t)(R > 0 ? R : 1) * sizeof(uint32_t), 256);
+}
+
+inline Workspace carve_workspace(void* base, int32_t T, int32_t E, int32_t k)
 {
     char* p = static_cast<char*>(base);
-    const size_t hb = ws_hist_bytes(R, E);
+    const size_t hb = ws_hist_bytes(T, E, k);
+    const size_t tb = align_up((size_t)E * sizeof(uint32_t), 256);
     Workspace w;
     w.hist_t = reinterpret_cast<uint32_t*>(p);
     w.prefix = reinterpret_cast<uint32_t*>(p + hb);
-    w.local_rank = reinterpret_cast<uint32_t*>(p + 2 * hb);
+    w.totals = reinterpret_cast<uint32_t*>(p + 2 * hb);
+    w.local_rank = reinterpret_cast<uint32_t*>(p + 2 * hb + tb);
     return w;
 }
 
-// Parts per row for the row kernels: enough wavefronts to fill the GPU, each part at least
-// `min_chunks` long and a multiple of `align` chunks.
-struct PartPlan {
-    int32_t parts;
-    int32_t chunks_per_part;
-};
-
-inline PartPlan part_plan(int64_t R, int32_t chunks_per_row, int32_t align, int32_t min_chunks)
+inline int64_t xcd_blocks(int32_t T, int64_t items_per_token, int waves_per_group)
 {
-    int64_t parts = R > 0 ? ceil_div(kTargetWaves, R) : 1;
-    const int64_t max_parts = ceil_div(chunks_per_row, min_chunks);
-    if (parts > max_parts)
-        parts = max_parts;
-    if (parts < 1)
-        parts = 1;
-    int64_t cpp = ceil_div(chunks_per_row, parts);
-    cpp = ceil_div(cpp, align) * align;
-    PartPlan p;
-    p.chunks_per_part = (int32_t)cpp;
-    p.parts = (int32_t)ceil_div(chunks_per_row, cpp);
-    return p;
-}
-
-inline dim3 xcd_grid(int32_t T, int64_t items_per_token, int waves_per_group)
-{
-    const int64_t per_xcd = ceil_div(ceil_div(T, kXcds) * items_per_token, waves_per_group);
-    return dim3((unsigned)(per_xcd * kXcds));
+    return ceil_div(ceil_div(T, kXcds) * items_per_token, waves_per_group) * kXcds;
 }
 
 inline moe_status_t launch_status()
@@ -902,90 +882,134 @@ moe_status_t check_pack_args(const void* x, moe_dtype_t x_dtype, int32_t T, int3
     return MOE_OK;
 }
 
-template <int EPW>
-void launch_counts_epw(const int32_t* topk_idx, int64_t R, int32_t E, int32_t n_ranks,
-                       const moe_dispatch_out_t* out, const Workspace& ws, const LayoutPlan& plan,
-                       hipStream_t stream)
+moe_status_t check_route_args(const float* logits, int32_t T, int32_t E, int32_t k,
+                              const int32_t* topk_idx, const float* topk_w)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK)
+        return MOE_ERR_UNSUPPORTED;
+    if (T > 0 && (!logits || !topk_idx || !topk_w))
+        return MOE_ERR_INVALID;
+    if ((int64_t)T * k > INT32_MAX)
+        return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+#define MOE_ROUTE_LAUNCH(KERNEL, GRID, BLOCK, LDS, ...)                                          \
+    do {                                                                                          \
+        const int pl_ = (int)ceil_div(E, 64);                                                     \
+        if (pl_ <= 1)                                                                             \
+            KERNEL<1><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (pl_ <= 2)                                                                        \
+            KERNEL<2><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (pl_ <= 4)                                                                        \
+            KERNEL<4><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (pl_ <= 6)                                                                        \
+            KERNEL<6><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (pl_ <= 8)                                                                        \
+            KERNEL<8><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else                                                                                      \
+            KERNEL<16><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                \
+    } while (0)
+
+void launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                  float* topk_w, hipStream_t stream)
+{
+    const dim3 grid((unsigned)ceil_div(T, kWaves));
+    MOE_ROUTE_LAUNCH(k_route_topk, grid, kThreads, 0, logits, T, E, k, topk_idx, topk_w);
+}
+
+void launch_route_layout(const float* logits, int32_t T, int32_t E, int32_t k,
+                         int32_t* topk_idx, float* topk_w, const Workspace& ws,
+                         const LayoutPlan& plan, hipStream_t stream)
+{
+    const dim3 grid((unsigned)plan.nblk);
+    const size_t lds = (size_t)E * sizeof(uint32_t);
+    MOE_ROUTE_LAUNCH(k_route_layout, grid, kGroupThreads, lds, logits, T, E, k, plan.nblk,
+                     topk_idx, topk_w, ws.hist_t, ws.local_rank);
+}
+
+void launch_hist(const int32_t* topk_idx, int64_t R, int32_t E, const Workspace& ws,
+                 const LayoutPlan& plan, hipStream_t stream)
 {
     if (plan.nblk > 0)
         k_layout_hist<<<plan.nblk, kThreads, hist_lds_bytes(E), stream>>>(
             topk_idx, (int32_t)R, E, plan.rows_per_block, plan.nblk, ws.hist_t, ws.local_rank);
-    k_layout_scan<EPW><<<1, kScanThreads, 0, stream>>>(ws.hist_t, E, n_ranks, plan.nblk,
-                                                       ws.prefix, out->expert_counts,
-                                                       out->expert_offsets, out->rank_counts,
-                                                       out->rank_offsets);
 }
 
-// The counting half of dispatch: histograms, scan, counts and offsets. With T = 0 only the scan
-// runs, which writes zero counts.
-void launch_layout_counts(const int32_t* topk_idx, int64_t R, int32_t E, int32_t n_ranks,
-                          const moe_dispatch_out_t* out, const Workspace& ws,
-                          const LayoutPlan& plan, hipStream_t stream)
+CountOutputs count_outputs(const moe_dispatch_out_t* out, int32_t n_ranks)
 {
-    const int64_t epw = ceil_div(E, kScanThreads / 64);
-    if (epw <= 8)
-        launch_counts_epw<8>(topk_idx, R, E, n_ranks, out, ws, plan, stream);
-    else if (epw <= 16)
-        launch_counts_epw<16>(topk_idx, R, E, n_ranks, out, ws, plan, stream);
-    else if (epw <= 32)
-        launch_counts_epw<32>(topk_idx, R, E, n_ranks, out, ws, plan, stream);
+    CountOutputs co;
+    co.expert_counts = out->expert_counts;
+    co.expert_offsets = out->expert_offsets;
+    co.rank_counts = out->rank_counts;
+    co.rank_offsets = out->rank_offsets;
+    co.N = n_ranks;
+    return co;
+}
+
+// Scan of the histograms, then the rows (whose workgroup 0 also writes the count outputs, so it
+// runs even for an empty batch).
+void launch_scan_rows(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E,
+                      const moe_dispatch_out_t* out, int32_t n_ranks, const Workspace& ws,
+                      const LayoutPlan& plan, hipStream_t stream)
+{
+    const dim3 grid((unsigned)ceil_div(E, kGroupWaves));
+    const int64_t s = ceil_div(plan.nblk, 64);
+#define MOE_SCAN(SS)                                                                              \
+    k_expert_scan<SS><<<grid, kGroupThreads, 0, stream>>>(ws.hist_t, E, plan.nblk, ws.prefix,    \
+                                                          ws.totals)
+    if (s <= 1)
+        MOE_SCAN(1);
+    else if (s <= 2)
+        MOE_SCAN(2);
+    else if (s <= 4)
+        MOE_SCAN(4);
+    else if (s <= 8)
+        MOE_SCAN(8);
     else
-        launch_counts_epw<64>(topk_idx, R, E, n_ranks, out, ws, plan, stream);
-}
-
-RowPlan make_row_plan(const int32_t* topk_idx, const Workspace& ws, const LayoutPlan& plan,
-                      int32_t E, const moe_dispatch_out_t* out)
-{
+        MOE_SCAN(16);
+#undef MOE_SCAN
     RowPlan rp;
     rp.topk_idx = topk_idx;
     rp.local_rank = ws.local_rank;
     rp.prefix = ws.prefix;
-    rp.expert_offsets = out->expert_offsets;
+    rp.totals = ws.totals;
     rp.token_row = out->token_row;
     rp.row_token = out->row_token;
     rp.E = E;
     rp.nblk = plan.nblk;
     rp.rows_per_block = plan.rows_per_block;
-    return rp;
+    const int64_t want = ceil_div(R, kThreads);
+    const unsigned blocks = (unsigned)(want < 1 ? 1 : want < 4096 ? want : 4096);
+    k_layout_rows<<<blocks, kThreads, 0, stream>>>(rp, R, k, count_outputs(out, n_ranks));
 }
 
-template <bool PLANNED>
 void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t k,
-                 const RowPlan& rp, moe_dtype_t payload_dtype, void* recv, float* recv_scales,
-                 hipStream_t stream)
+                 const int32_t* token_row, moe_dtype_t payload_dtype, void* recv,
+                 float* recv_scales, hipStream_t stream)
 {
     const int32_t R = T * k;
+    if (R == 0)
+        return;
     if (payload_dtype != MOE_FP8_E4M3) {
         const int32_t cpr = (int32_t)((int64_t)H * (int64_t)dtype_size(x_dtype) / 16);
-        const PartPlan pp = part_plan(R, cpr, 1, 64);
-        const dim3 grid = xcd_grid(T, (int64_t)k * pp.parts, kPackWaves);
-        const u32x4* xs = static_cast<const u32x4*>(x);
-        u32x4* rv = static_cast<u32x4*>(recv);
-        const int64_t u = ceil_div(pp.chunks_per_part, 64);
-#define MOE_PACK(UU)                                                                              \
-    k_pack_rows<UU, PLANNED><<<grid, 64 * kPackWaves, 0, stream>>>(xs, T, k, R, cpr, pp.parts,   \
-                                                                   pp.chunks_per_part, rp, rv)
-        if (u <= 1)
-            MOE_PACK(1);
-        else if (u <= 2)
-            MOE_PACK(2);
-        else if (u <= 4)
-            MOE_PACK(4);
-        else if (u <= 8)
-            MOE_PACK(8);
-        else
-            MOE_PACK(16);
-#undef MOE_PACK
+        const int32_t pieces = (int32_t)ceil_div(cpr, 64);
+        const dim3 grid((unsigned)xcd_blocks(T, (int64_t)k * pieces, kPackWaves));
+        k_pack_rows<<<grid, 64 * kPackWaves, 0, stream>>>(static_cast<const u32x4*>(x), T, k, R,
+                                                          cpr, pieces, token_row,
+                                                          static_cast<u32x4*>(recv));
     } else {
-        const PartPlan pp = part_plan(R, H / 8, 16, 64);
-        const dim3 grid = xcd_grid(T, (int64_t)k * pp.parts, kPackWaves);
+        const int32_t pieces = (int32_t)ceil_div(H / 8, 64);
+        const dim3 grid((unsigned)xcd_blocks(T, (int64_t)k * pieces, kPackWaves));
         if (x_dtype == MOE_F32)
-            k_pack_rows_fp8<float, PLANNED><<<grid, 64 * kPackWaves, 0, stream>>>(
-                static_cast<const float*>(x), T, H, k, R, pp.parts, pp.chunks_per_part, rp,
+            k_pack_rows_fp8<float><<<grid, 64 * kPackWaves, 0, stream>>>(
+                static_cast<const float*>(x), T, H, k, R, pieces, token_row,
                 static_cast<uint8_t*>(recv), recv_scales);
         else
-            k_pack_rows_fp8<uint16_t, PLANNED><<<grid, 64 * kPackWaves, 0, stream>>>(
-                static_cast<const uint16_t*>(x), T, H, k, R, pp.parts, pp.chunks_per_part, rp,
+            k_pack_rows_fp8<uint16_t><<<grid, 64 * kPackWaves, 0, stream>>>(
+                static_cast<const uint16_t*>(x), T, H, k, R, pieces, token_row,
                 static_cast<uint8_t*>(recv), recv_scales);
     }
 }
@@ -1034,33 +1058,12 @@ const char* moe_status_str(moe_status_t status)
 moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                             int32_t* topk_idx, float* topk_w, hipStream_t stream)
 {
-    if (T < 0 || E < 1 || k < 1 || k > E)
-        return MOE_ERR_INVALID;
-    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK)
-        return MOE_ERR_UNSUPPORTED;
-    if (T > 0 && (!logits || !topk_idx || !topk_w))
-        return MOE_ERR_INVALID;
-    if ((int64_t)T * k > INT32_MAX)
-        return MOE_ERR_INVALID;
+    const moe_status_t st = check_route_args(logits, T, E, k, topk_idx, topk_w);
+    if (st != MOE_OK)
+        return st;
     if (T == 0)
         return MOE_OK;
-    const int pl = (E + 63) / 64;
-    const dim3 grid((unsigned)ceil_div(T, kWaves));
-#define MOE_ROUTE(PP)                                                                             \
-    k_route_topk<PP><<<grid, kThreads, 0, stream>>>(logits, T, E, k, topk_idx, topk_w)
-    if (pl <= 1)
-        MOE_ROUTE(1);
-    else if (pl <= 2)
-        MOE_ROUTE(2);
-    else if (pl <= 4)
-        MOE_ROUTE(4);
-    else if (pl <= 6)
-        MOE_ROUTE(6);
-    else if (pl <= 8)
-        MOE_ROUTE(8);
-    else
-        MOE_ROUTE(16);
-#undef MOE_ROUTE
+    launch_route(logits, T, E, k, topk_idx, topk_w, stream);
     return launch_status();
 }
 
@@ -1068,8 +1071,7 @@ size_t moe_dispatch_workspace_bytes(int32_t T, int32_t E, int32_t k)
 {
     if (T < 0 || E < 1 || k < 1 || (int64_t)T * k > INT32_MAX)
         return 0;
-    const int64_t R = (int64_t)T * k;
-    return ws_bytes(R, E);
+    return ws_bytes(T, E, k);
 }
 
 moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
@@ -1084,15 +1086,10 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, 
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)T * k;
-    const LayoutPlan plan = layout_plan(R);
-    const Workspace ws = carve_workspace(workspace, R, E);
-    launch_layout_counts(topk_idx, R, E, n_ranks, out, ws, plan, stream);
-    if (R > 0) {
-        const RowPlan rp = make_row_plan(topk_idx, ws, plan, E, out);
-        const int64_t want = ceil_div(R, kThreads);
-        const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
-        k_layout_rows<<<blocks, kThreads, 0, stream>>>(rp, (int32_t)R, k);
-    }
+    const LayoutPlan plan = hist_plan(R);
+    const Workspace ws = carve_workspace(workspace, T, E, k);
+    launch_hist(topk_idx, R, E, ws, plan, stream);
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, stream);
     return launch_status();
 }
 
@@ -1106,9 +1103,7 @@ moe_status_t moe_dispatch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, in
         return st;
     if (T == 0)
         return MOE_OK;
-    RowPlan rp = {};
-    rp.token_row = const_cast<int32_t*>(token_row);   // read only on this path
-    launch_pack<false>(x, x_dtype, T, H, k, rp, payload_dtype, recv, recv_scales, stream);
+    launch_pack(x, x_dtype, T, H, k, token_row, payload_dtype, recv, recv_scales, stream);
     return launch_status();
 }
 
@@ -1129,14 +1124,50 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)T * k;
-    const LayoutPlan plan = layout_plan(R);
-    const Workspace ws = carve_workspace(workspace, R, E);
-    launch_layout_counts(topk_idx, R, E, n_ranks, out, ws, plan, stream);
-    if (R > 0) {
-        const RowPlan rp = make_row_plan(topk_idx, ws, plan, E, out);
-        launch_pack<true>(x, x_dtype, T, H, k, rp, payload_dtype, out->recv, out->recv_scales,
-                          stream);
+    const LayoutPlan plan = hist_plan(R);
+    const Workspace ws = carve_workspace(workspace, T, E, k);
+    launch_hist(topk_idx, R, E, ws, plan, stream);
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, stream);
+    launch_pack(x, x_dtype, T, H, k, out->token_row, payload_dtype, out->recv, out->recv_scales,
+                stream);
+    return launch_status();
+}
+
+moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t x_dtype,
+                                int32_t T, int32_t H, int32_t E, int32_t k, int32_t n_ranks,
+                                moe_dtype_t payload_dtype, int32_t* topk_idx, float* topk_w,
+                                const moe_dispatch_out_t* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    moe_status_t st = check_route_args(logits, T, E, k, topk_idx, topk_w);
+    if (st != MOE_OK)
+        return st;
+    st = check_layout_args(topk_idx, T, k, E, n_ranks, out);
+    if (st != MOE_OK)
+        return st;
+    st = check_pack_args(x, x_dtype, T, H, k, out->token_row, payload_dtype, out->recv,
+                         out->recv_scales);
+    if (st != MOE_OK)
+        return st;
+    if (!workspace || workspace_bytes < moe_dispatch_workspace_bytes(T, E, k))
+        return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t R = (int64_t)T * k;
+    const Workspace ws = carve_workspace(workspace, T, E, k);
+    LayoutPlan plan;
+    if (T > 0 && fused_route_fits(T)) {
+        plan = route_plan(T, k);
+        launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan, stream);
+    } else {
+        plan = hist_plan(R);
+        if (T > 0)
+            launch_route(logits, T, E, k, topk_idx, topk_w, stream);
+        launch_hist(topk_idx, R, E, ws, plan, stream);
     }
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, stream);
+    launch_pack(x, x_dtype, T, H, k, out->token_row, payload_dtype, out->recv, out->recv_scales,
+                stream);
     return launch_status();
 }
 

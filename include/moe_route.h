@@ -72,8 +72,9 @@ moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k
                             int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
 /*
- * Bytes of device workspace that moe_dispatch / moe_dispatch_layout need for (T, E, k): per-block
- * expert histograms, their in-expert prefixes and per-item ranks. Returns 0 for invalid sizes.
+ * Bytes of device workspace that moe_dispatch, moe_dispatch_layout and moe_route_dispatch need for
+ * (T, E, k): per-block expert histograms, their in-expert prefixes, expert totals and per-item
+ * ranks. Returns 0 for invalid sizes.
  * The workspace needs no initialisation and holds nothing the caller uses afterwards. Two calls
  * that may run at the same time (different streams) must not share a workspace.
  */
@@ -134,6 +135,21 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
                           const int32_t* topk_idx, int32_t k, int32_t E, int32_t n_ranks,
                           moe_dtype_t payload_dtype, const moe_dispatch_out_t* out,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_route_dispatch -- moe_route_topk followed by moe_dispatch on the same stream: the router's
+ * choice ("Introductie") and the dispatch of every token to its experts' rows ("Dispatch en
+ * Combine"), with the counting of each group of tokens done in the same launch as their routing.
+ *   logits [T, E] fp32 as for moe_route_topk; topk_idx [T, k] and topk_w [T, k] are written as
+ *   moe_route_topk writes them; x, x_dtype, H, n_ranks, payload_dtype, out and the workspace are
+ *   as for moe_dispatch. Every output equals what the two calls write.
+ * Argument errors are those of the two calls.
+ */
+moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t x_dtype,
+                                int32_t T, int32_t H, int32_t E, int32_t k, int32_t n_ranks,
+                                moe_dtype_t payload_dtype, int32_t* topk_idx, float* topk_w,
+                                const moe_dispatch_out_t* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_combine -- weighted sum of the returned rows of every token ("Dispatch en Combine": the

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["moe_combine", "moe_dispatch", "moe_dispatch_layout",
                             "moe_dispatch_pack", "moe_dispatch_workspace_bytes",
-                            "moe_route_topk", "moe_status_str"])
+                            "moe_route_dispatch", "moe_route_topk", "moe_status_str"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -70,10 +70,13 @@ def test_workspace_bytes():
     assert ws(-1, 8, 2) == 0 and ws(4, 0, 2) == 0 and ws(4, 8, 0) == 0
     assert ws(2 ** 30, 8, 4) == 0
     assert ws(0, 8, 2) > 0
-    # histogram and its scan (<= 64 blocks x E u32 each) plus one u32 rank per row, in
-    # 256-byte aligned pieces
+    # histogram and its prefixes (E u32 per block each: at most 64 blocks of caller ids, or one
+    # block per 16 routed tokens), the E expert totals and one u32 rank per row, in 256-byte
+    # aligned pieces
     R = 4096 * 8
-    assert R * 4 <= ws(4096, 384, 8) <= R * 4 + 2 * (64 * 384 + 1) * 4 + 768
+    nblk = 4096 // 16
+    assert R * 4 <= ws(4096, 384, 8) <= R * 4 + 2 * (nblk * 384 + 1) * 4 + 384 * 4 + 1024
+    assert ws(4096, 384, 8) >= R * 4 + 2 * nblk * 384 * 4 + 384 * 4
     assert ws(4096, 384, 8) % 256 == 0
     assert ws(128, 256, 8) >= 128 * 8 * 4
 
@@ -139,6 +142,35 @@ def test_dispatch_validation_checks_both_halves():
              S0) == moe.MOE_ERR_UNSUPPORTED                                       # recv align
     assert f(A16, BF16, 4, 256, A16, 2, 8, 2, BF16, ctypes.byref(o), A16, need - 4,
              S0) == moe.MOE_ERR_WORKSPACE
+
+
+def test_route_dispatch_validation_checks_every_part():
+    f = moe.load().moe_route_dispatch
+    o = _out_struct()
+    BF16, FP8 = moe.MOE_BF16, moe.MOE_FP8_E4M3
+    need = moe.moe_dispatch_workspace_bytes(4, 8, 2)
+    args = dict(logits=A16, x=A16, xd=BF16, T=4, H=256, E=8, k=2, N=2, pd=BF16, idx=A16b,
+                w=A16b, out=ctypes.byref(o), ws=A16, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["logits"], a["x"], a["xd"], a["T"], a["H"], a["E"], a["k"], a["N"], a["pd"],
+                 a["idx"], a["w"], a["out"], a["ws"], a["wsb"], S0)
+
+    assert call(k=9) == moe.MOE_ERR_INVALID                      # k > E
+    assert call(logits=None) == moe.MOE_ERR_INVALID
+    assert call(idx=None) == moe.MOE_ERR_INVALID
+    assert call(w=None) == moe.MOE_ERR_INVALID
+    assert call(E=2048) == moe.MOE_ERR_UNSUPPORTED
+    assert call(N=3) == moe.MOE_ERR_INVALID                      # E % N
+    assert call(out=None) == moe.MOE_ERR_INVALID
+    assert call(x=MIS) == moe.MOE_ERR_UNSUPPORTED
+    assert call(H=192, pd=FP8) == moe.MOE_ERR_UNSUPPORTED        # H % 128 for fp8
+    o2 = _out_struct(recv_scales=None)
+    assert call(pd=FP8, out=ctypes.byref(o2)) == moe.MOE_ERR_INVALID
+    assert call(wsb=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=None) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=MIS) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_combine_validation():

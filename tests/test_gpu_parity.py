@@ -92,33 +92,57 @@ def test_combine(name):
 
 
 @pytest.mark.parametrize("name", ORDER)
+def test_route_dispatch(name):
+    """The fused entry point writes what the oracle's route and dispatch write."""
+    w = WORKLOADS[name]
+    _announce(f"route_dispatch {name} T={w.T} H={w.H} E={w.E} k={w.k} N={w.N}")
+    inp, idx, wt, d, *_ = oracle_chain(name)
+    buf = moe.alloc_dispatch_out(w.T, w.H, w.E, w.k, w.N, w.payload)
+    ws = moe.alloc_workspace(w.T, w.E, w.k)
+    g_idx, g_w, _ = moe.moe_route_dispatch(to_dev(inp["logits"], "f32"),
+                                           to_dev(inp["x"], w.x_dtype), w.k, w.N, buf, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(g_idx), idx)
+    _check_weights(to_host(g_w), wt)
+    _check_layout(buf, d)
+    _check_payload(buf, d, w.payload)
+
+
+@pytest.mark.parametrize("name", ORDER)
 def test_full_chain_and_determinism(name):
-    """Route -> dispatch -> combine all on the GPU (the GPU's own weights and row maps), twice."""
+    """Route -> dispatch -> combine on the GPU (its own weights and row maps) three times: separate
+    route and dispatch calls, then the fused call twice on one reused, already written
+    workspace. All three must agree byte for byte and with the oracle."""
     w = WORKLOADS[name]
     _announce(f"chain {name}")
     inp, idx, wt, d, y, out = oracle_chain(name)
     x = to_dev(inp["x"], w.x_dtype)
     logits = to_dev(inp["logits"], "f32")
     y_dev = to_dev(y, w.y_dtype)
+    ws = moe.alloc_workspace(w.T, w.E, w.k)
     results = []
-    for _ in range(2):
-        g_idx, g_w = moe.moe_route_topk(logits, w.k)
+    for run in range(3):
         buf = moe.alloc_dispatch_out(w.T, w.H, w.E, w.k, w.N, w.payload)
-        ws = moe.alloc_workspace(w.T, w.E, w.k)
-        moe.moe_dispatch(x, g_idx, w.E, w.N, buf, ws)
+        if run == 0:
+            g_idx, g_w = moe.moe_route_topk(logits, w.k)
+            moe.moe_dispatch(x, g_idx, w.E, w.N, buf, ws)
+        else:
+            g_idx, g_w, _ = moe.moe_route_dispatch(logits, x, w.k, w.N, buf, ws)
         res = torch.empty((w.T, w.H), dtype=moe.TORCH_DTYPES[w.out_dtype], device="cuda")
         moe.moe_combine(y_dev, buf.token_row, g_w, res)
         torch.cuda.synchronize()
         results.append((to_host(g_idx), to_host(g_w), to_host(buf.recv), to_host(buf.token_row),
-                        to_host(res)))
-    a, b = results
-    for u, v in zip(a, b):
-        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "two runs differ"
-    g_idx, g_w, recv, token_row, res = a
+                        to_host(buf.row_token), to_host(buf.expert_offsets), to_host(res)))
+    for other in results[1:]:
+        for u, v in zip(results[0], other):
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "runs differ"
+    g_idx, g_w, recv, token_row, row_token, expert_offsets, res = results[0]
     assert np.array_equal(g_idx, idx)
     _check_weights(g_w, wt)
     assert np.array_equal(recv, d["recv"])
     assert np.array_equal(token_row, d["token_row"])
+    assert np.array_equal(row_token, d["row_token"])
+    assert np.array_equal(expert_offsets, d["expert_offsets"])
     assert_close_out(res, out, w.out_dtype)
 
 
@@ -134,6 +158,8 @@ EDGE = [
     (4500, 512, 256, 8, 16, "bf16", "bf16"),    # T*k = 36000: several rows per layout block
     (9000, 256, 1024, 8, 64, "bf16", "bf16"),   # E at its maximum; T*k = 72000 > 64 * 1024
     (3, 128, 1024, 64, 1024, "bf16", "fp8_e4m3"),   # k at its maximum, N = E = 1024
+    (16384, 128, 64, 2, 4, "bf16", "bf16"),     # most tokens the fused route-layout takes
+    (16401, 128, 64, 2, 4, "f32", "f32"),       # one token more: separate route + histogram
 ]
 
 
@@ -164,6 +190,14 @@ def test_edge_shapes(T, H, E, k, N, x_dtype, payload):
         _check_layout(buf, d)
         _check_payload(buf, d, payload)
         assert_close_out(to_host(res), out, out_dtype)
+    buf = moe.alloc_dispatch_out(T, H, E, k, N, payload)
+    g_idx, g_w, _ = moe.moe_route_dispatch(to_dev(inp["logits"], "f32"), to_dev(inp["x"], x_dtype),
+                                           k, N, buf, moe.alloc_workspace(T, E, k))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(g_idx), idx)
+    _check_weights(to_host(g_w), wt)
+    _check_layout(buf, d)
+    _check_payload(buf, d, payload)
 
 
 def test_all_tokens_on_one_expert_and_ties():
@@ -176,14 +210,20 @@ def test_all_tokens_on_one_expert_and_ties():
     x = np.random.default_rng(0).standard_normal((T, H)).astype(np.float32)
     idx, wt = oracle.route(logits, k)
     d = oracle.dispatch(x, "f32", idx, E, N, "f32")
-    g_idx, g_w = moe.moe_route_topk(to_dev(logits, "f32"), k)
-    buf = moe.alloc_dispatch_out(T, H, E, k, N, "f32")
-    moe.moe_dispatch(to_dev(x, "f32"), g_idx, E, N, buf, moe.alloc_workspace(T, E, k))
-    torch.cuda.synchronize()
-    assert np.array_equal(to_host(g_idx), idx)
-    _check_weights(to_host(g_w), wt)
-    _check_layout(buf, d)
-    _check_payload(buf, d, "f32")
+    for fused in (False, True):
+        buf = moe.alloc_dispatch_out(T, H, E, k, N, "f32")
+        ws = moe.alloc_workspace(T, E, k)
+        if fused:
+            g_idx, g_w, _ = moe.moe_route_dispatch(to_dev(logits, "f32"), to_dev(x, "f32"), k, N,
+                                                   buf, ws)
+        else:
+            g_idx, g_w = moe.moe_route_topk(to_dev(logits, "f32"), k)
+            moe.moe_dispatch(to_dev(x, "f32"), g_idx, E, N, buf, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(g_idx), idx)
+        _check_weights(to_host(g_w), wt)
+        _check_layout(buf, d)
+        _check_payload(buf, d, "f32")
 
 
 def test_duplicate_expert_ids_in_a_token():
@@ -230,6 +270,13 @@ def test_zero_tokens_writes_zero_counts():
     moe.moe_dispatch(torch.empty((0, 128), dtype=torch.bfloat16, device="cuda"),
                      torch.empty((0, k), dtype=torch.int32, device="cuda"), E, N, buf,
                      moe.alloc_workspace(0, E, k))
+    torch.cuda.synchronize()
+    for t in (buf.expert_counts, buf.expert_offsets, buf.rank_counts, buf.rank_offsets):
+        assert np.all(to_host(t) == 0)
+        t.fill_(-7)
+    moe.moe_route_dispatch(torch.empty((0, E), dtype=torch.float32, device="cuda"),
+                           torch.empty((0, 128), dtype=torch.bfloat16, device="cuda"), k, N, buf,
+                           moe.alloc_workspace(0, E, k))
     torch.cuda.synchronize()
     for t in (buf.expert_counts, buf.expert_offsets, buf.rank_counts, buf.rank_offsets):
         assert np.all(to_host(t) == 0)

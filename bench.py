@@ -46,6 +46,9 @@ def parse_args():
                    help="host time budget of the CPU-oracle baseline (0 disables it)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run the 1 GiB plain copy kernel (for HBM counter calibration)")
+    p.add_argument("--other-workloads", type=int, default=1,
+                   help="also time the step on the other workloads (tiny, decode, decode_fp8, "
+                        "skewed); 0 skips them")
     return p.parse_args()
 
 
@@ -215,6 +218,64 @@ def _cpu_model():
     return platform.processor()
 
 
+def timed(torch, sets, phases, K, per_call_events):
+    """K steps of `phases` (rotating over the buffer sets) between two HIP events on the launch
+    stream; with per_call_events, also an event after every call (each costs a few us of GPU
+    idle, so the headline loop records none). Returns (ms per step, {phase: us} or None,
+    per-step ms list or None)."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+          for _ in range(K)] if per_call_events else None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        s = sets[i % len(sets)]
+        if ev is None:
+            for ph in phases:
+                s[ph]()
+        else:
+            e = ev[i]
+            e[0].record()
+            for p, ph in enumerate(phases):
+                s[ph]()
+                e[p + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    per = steps = None
+    if ev is not None:
+        per = {ph: sum(ev[i][p].elapsed_time(ev[i][p + 1]) for i in range(K)) / K * 1e3
+               for p, ph in enumerate(phases)}
+        steps = [ev[i][0].elapsed_time(ev[i][-1]) for i in range(K)]
+    return start.elapsed_time(end) / K, per, steps
+
+
+HEADLINE = ("route_dispatch", "combine")
+
+
+def other_workloads(torch, moe, dev, names, K):
+    """The headline step on the smaller workloads (latency-bound ones are reported in us)."""
+    from combine_moe_route_03_amd.workloads import WORKLOADS, make_inputs
+    res = {}
+    for name in names:
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        sets = [make_set(w, inp, dev, moe, torch) for _ in range(2)]
+        for i in range(10):
+            for ph in HEADLINE:
+                sets[i % 2][ph]()
+        ms, _, _ = timed(torch, sets, HEADLINE, K, False)
+        _, per, steps = timed(torch, sets, HEADLINE, K, True)
+        alg = sum(algorithmic_bytes(w).values())
+        res[name] = {"us_per_step": round(ms * 1e3, 2),
+                     "median_evented_us": round(sorted(steps)[len(steps) // 2] * 1e3, 2),
+                     "phases_us": {ph: round(v, 2) for ph, v in per.items()},
+                     "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+                     "shape": f"T={w.T} H={w.H} E={w.E} k={w.k} N={w.N} {w.payload}"}
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -244,34 +305,7 @@ def main():
     inp = make_inputs(w)
     sets = [make_set(w, inp, dev, moe, torch) for _ in range(max(1, args.sets))]
 
-    def timed(phases, K, per_call_events):
-        """K steps of `phases` between two HIP events; with per_call_events, also an event after
-        every call (each costs a few us of GPU idle, so the headline loop records none).
-        Returns (ms per step, {phase: us} or None)."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
-              for _ in range(K)] if per_call_events else None
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record()
-        for i in range(K):
-            s = sets[i % len(sets)]
-            if ev is None:
-                for ph in phases:
-                    s[ph]()
-            else:
-                e = ev[i]
-                e[0].record()
-                for p, ph in enumerate(phases):
-                    s[ph]()
-                    e[p + 1].record()
-        end.record()
-        torch.cuda.synchronize()
-        per = None if ev is None else {
-            ph: sum(ev[i][p].elapsed_time(ev[i][p + 1]) for i in range(K)) / K * 1e3
-            for p, ph in enumerate(phases)}
-        return start.elapsed_time(end) / K, per
-
-    headline = ("route_dispatch", "combine")
+    headline = HEADLINE
     separate = ("route", "dispatch", "combine")
     split = ("route", "layout", "pack", "combine")
     for i in range(args.warmup):
@@ -280,20 +314,23 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
     wall0 = time.perf_counter()
-    ms_per_step, _ = timed(headline, K, False)       # the headline: no events inside the step
+    ms_per_step, _, _ = timed(torch, sets, headline, K, False)   # the headline: no inner events
     wall = time.perf_counter() - wall0
-    ms_evented, phase_us = timed(headline, K, True)  # per-call times (events after every call)
-    ms_sep, sep_us = timed(separate, K, True)        # routing and dispatch as separate calls
-    ms_split, split_us = timed(split, K, True)       # packing kernel on its own
+    ms_evented, phase_us, steps_ev = timed(torch, sets, headline, K, True)   # per-call times
+    ms_sep, sep_us, _ = timed(torch, sets, separate, K, True)    # route, dispatch as two calls
+    ms_split, split_us, _ = timed(torch, sets, split, K, True)   # packing kernel on its own
+    ms_warm, _, _ = timed(torch, sets[:1], headline, K, False)   # one buffer set: warm caches
 
     alg = algorithmic_bytes(w)
     alg_total = sum(alg.values())
     value = alg_total / (ms_per_step * 1e-3) / 1e9
-    # The dominant kernel: packing (the same kernel in every dispatch entry point, timed alone
-    # through moe_dispatch_pack) or combine.
-    kernel_us = {"pack": split_us["pack"], "combine": phase_us["combine"]}
+    # The dominant kernel: packing (its token-order form, launched alone through moe_dispatch_pack;
+    # the dispatch entry points use the window-ordered form, seen in the kernel trace) or combine,
+    # each timed over K back-to-back launches of that kernel alone (two events around the loop),
+    # which is what a kernel trace averages.
+    kernel_us = {ph: timed(torch, sets, (ph,), K, False)[0] * 1e3 for ph in ("pack", "combine")}
     dominant = max(kernel_us, key=lambda ph: kernel_us[ph])
-    pattern = {"pack": r"k_pack_rows(_fp8<.*>)?", "combine": r"k_combine<.*>"}[dominant]
+    pattern = {"pack": r"k_pack_rows(_fp8)?<(.*, )?0>", "combine": r"k_combine<.*>"}[dominant]
     prof_name, traffic = hbm_traffic(pattern)
     kernel_name = prof_name or {"pack": "k_pack_rows" if w.payload != "fp8_e4m3"
                                 else "k_pack_rows_fp8", "combine": "k_combine"}[dominant]
@@ -307,6 +344,16 @@ def main():
           f" | split path {ms_split * 1e3:.1f} us/step: " +
           ", ".join(f"{ph} {v:.1f} us" for ph, v in split_us.items()) +
           f"; copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    others = None
+    if args.other_workloads:
+        del sets
+        torch.cuda.empty_cache()
+        print("[bench] other workloads", file=sys.stderr, flush=True)
+        others = other_workloads(torch, moe, dev, ("tiny", "decode", "decode_fp8", "skewed"),
+                                 100)
+        print("[bench] " + "; ".join(f"{n} {r['us_per_step']} us" for n, r in others.items()),
+              file=sys.stderr, flush=True)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -337,6 +384,8 @@ def main():
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "phases_us": {ph: round(v, 2) for ph, v in phase_us.items()},
         "evented_ms_per_step": round(ms_evented, 5),
+        "evented_median_us_per_step": round(sorted(steps_ev)[len(steps_ev) // 2] * 1e3, 2),
+        "warm_us_per_step": round(ms_warm * 1e3, 2),
         "separate_calls": {"ms_per_step": round(ms_sep, 5),
                            "phases_us": {ph: round(v, 2) for ph, v in sep_us.items()}},
         "split_path": {"ms_per_step": round(ms_split, 5),
@@ -348,7 +397,9 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg[dominant],
                      "avg_launch_us": round(kernel_us[dominant], 2)},
+        "kernel_alone_us": {ph: round(v, 2) for ph, v in kernel_us.items()},
         "copy_ceiling_GBps": round(ceiling["GBps"], 1),
+        "other_workloads": others,
         "wall_s_timed_loop": round(wall, 4),
         "cpu_baseline": cpu,
     }

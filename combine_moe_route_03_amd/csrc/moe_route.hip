@@ -137,6 +137,48 @@ __device__ __forceinline__ float max_row16_f32(float v)
     return v;
 }
 
+// Exclusive scan of one value per thread over the NT threads of the block; returns the prefix
+// and writes the block total to *total. `wave_tot` holds NT/64 words of LDS.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
+                                                         uint32_t* total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
+        if (lane >= d)
+            x += y;
+    }
+    if (lane == 63)
+        wave_tot[wave] = x;
+    __syncthreads();
+    uint32_t base = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t s = wave_tot[w];
+        base += (w < wave) ? s : 0u;
+        all += s;
+    }
+    *total = all;
+    return base + x - v;
+}
+
+// Inclusive prefix sum over the 64 lanes (all active): row_shr 1, 2, 4, 8 within 16-lane rows
+// (lanes that would read before their row get 0), then row_bcast:15 and row_bcast:31 carry row
+// totals into the following rows.
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // bcast:31
+    return v;
+}
+
 // ---------------------------------------------------------------------------------- routing --
 // Selection key: larger logit first, equal logits to the lower id. The float is mapped to an
 // unsigned integer with the same order (sign-magnitude to offset binary; -0 folded onto +0) and
@@ -156,18 +198,18 @@ __device__ __forceinline__ float route_key_logit(uint64_t key)
     return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
-// Maximum over all 64 lanes (all active), the same value in every lane.
+// Maximum over all 64 lanes (all active), the same value in every lane: the maximum within each
+// 16-lane row (every lane of the row ends with it), then row_bcast:15 and row_bcast:31 carry row
+// maxima forward so lane 63 holds the wave's, and one readlane broadcasts it.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     v = max(v, dpp_u32<kDppQuadXor1>(v));
     v = max(v, dpp_u32<kDppQuadXor2>(v));
     v = max(v, dpp_u32<kDppRowHalfMirror>(v));
     v = max(v, dpp_u32<kDppRowMirror>(v));
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-    return max(max(a, b), max(c, d));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Top-k of one token by one whole wavefront (all lanes active). Lane l holds experts l, l+64, ...
@@ -251,12 +293,12 @@ __global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict
 // 16b .. 16b+15 (wavefront w takes token 16b + w); each selected (token, slot) sets bit w of
 // the LDS mask of its expert. A token's k experts are distinct, so the rank of (token, slot)
 // among the workgroup's items of the same expert, in (token, slot) order, is the number of bits
-// below w, and the workgroup's count of expert e is popcount(mask[e]), stored expert-major at
-// hist_t[e * nblk + b]. LDS: mask [E] u32.
+// below w, and the workgroup's count of expert e is popcount(mask[e]), stored block-major at
+// hist[b * E + e] (one coalesced row per workgroup). LDS: mask [E] u32.
 template <int PL>
 __global__ __launch_bounds__(kGroupThreads) void k_route_layout(
-    const float* __restrict__ logits, int32_t T, int32_t E, int32_t k, int32_t nblk,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ hist_t,
+    const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ hist,
     uint32_t* __restrict__ local_rank)
 {
     extern __shared__ uint32_t lds_mask[];
@@ -275,7 +317,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_layout(
     if (my_id >= 0)
         local_rank[t * k + lane] = (uint32_t)__popc(lds_mask[my_id] & ((1u << wave) - 1u));
     for (int e = tid; e < E; e += kGroupThreads)
-        hist_t[(int64_t)e * nblk + blockIdx.x] = (uint32_t)__popc(lds_mask[e]);
+        hist[(int64_t)blockIdx.x * E + e] = (uint32_t)__popc(lds_mask[e]);
 }
 
 // --------------------------------------------------------------------------------- layout --
@@ -288,11 +330,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_layout(
 //   run[e] + (bits of e in lower wavefronts) + (bits of e in lower lanes of its own wavefront),
 // which keeps index order without any atomic deciding a position. The first item of each expert
 // in the group then advances run[e] and clears the masks. The block's counts go to
-// hist_t[e * nblk + b] (expert-major). LDS: masks [4][E] u64, run [E] u32.
+// hist[b * E + e] (block-major, one coalesced row). LDS: masks [4][E] u64, run [E] u32.
 __global__ __launch_bounds__(kThreads) void k_layout_hist(const int32_t* __restrict__ topk_idx,
                                                           int32_t R, int32_t E,
-                                                          int32_t rows_per_block, int32_t nblk,
-                                                          uint32_t* __restrict__ hist_t,
+                                                          int32_t rows_per_block,
+                                                          uint32_t* __restrict__ hist,
                                                           uint32_t* __restrict__ local_rank)
 {
     extern __shared__ uint64_t lds_u64[];
@@ -341,57 +383,16 @@ __global__ __launch_bounds__(kThreads) void k_layout_hist(const int32_t* __restr
             local_rank[i] = rank;
     }
     for (int e = tid; e < E; e += kThreads)
-        hist_t[(int64_t)e * nblk + blockIdx.x] = run[e];
-}
-
-// Exclusive scan of one value per thread over the NT threads of the block; returns the prefix
-// and writes the block total to *total. `wave_tot` holds NT/64 words of LDS.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
-                                                         uint32_t* total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
-        if (lane >= d)
-            x += y;
-    }
-    if (lane == 63)
-        wave_tot[wave] = x;
-    __syncthreads();
-    uint32_t base = 0u, all = 0u;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const uint32_t s = wave_tot[w];
-        base += (w < wave) ? s : 0u;
-        all += s;
-    }
-    *total = all;
-    return base + x - v;
-}
-
-// Inclusive prefix sum over the 64 lanes (all active): row_shr 1, 2, 4, 8 within 16-lane rows
-// (lanes that would read before their row get 0), then row_bcast:15 and row_bcast:31 carry row
-// totals into the following rows.
-__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v)
-{
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // bcast:15
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // bcast:31
-    return v;
+        hist[(int64_t)blockIdx.x * E + e] = run[e];
 }
 
 // Scan of the block histograms, one wavefront per expert e (16 per workgroup, many workgroups).
-// Lane l holds the counts of blocks l*S .. l*S+S-1 of e's expert-major row; a wave scan of the
-// lane sums gives prefix[e * nblk + b] = rows of e in blocks before b, and e's total goes to
-// totals[e]. Requires nblk <= 64 * S (nblk = 0 gives zero totals).
+// Lane l gathers the counts of e in blocks l*S .. l*S+S-1 (the 16 wavefronts of a workgroup read
+// neighbouring words of the same block rows); a wave scan of the lane sums gives
+// prefix[e * nblk + b] = rows of e in blocks before b, and e's total goes to totals[e].
+// Requires nblk <= 64 * S (nblk = 0 gives zero totals).
 template <int S>
-__global__ __launch_bounds__(kGroupThreads) void k_expert_scan(const uint32_t* __restrict__ hist_t,
+__global__ __launch_bounds__(kGroupThreads) void k_expert_scan(const uint32_t* __restrict__ hist,
                                                                int32_t E, int32_t nblk,
                                                                uint32_t* __restrict__ prefix,
                                                                uint32_t* __restrict__ totals)
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_expert_scan(const uint32_t* _
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int b = lane * S + s;
-        c[s] = b < nblk ? hist_t[(int64_t)e * nblk + b] : 0u;
+        c[s] = b < nblk ? hist[(int64_t)b * E + e] : 0u;
         sum += c[s];
     }
     const uint32_t incl = wave_inclusive_scan_u32(sum);
@@ -431,6 +432,10 @@ struct CountOutputs {
     int32_t N;
 };
 
+// Packing windows. A window is `blocks_per_window` consecutive layout blocks, sized so that the
+// x rows of its tokens fit in one XCD's L2. For every window the rows kernel lists the window's
+// (row, token) pairs in ascending row order: list[w0 + q] is the q-th smallest destination row
+// of the window that starts at item w0 (entries past the window's valid rows hold (-1, -1)).
 struct RowPlan {
     const int32_t* topk_idx;
     const uint32_t* local_rank;
@@ -438,37 +443,61 @@ struct RowPlan {
     const uint32_t* totals;
     int32_t* token_row;
     int32_t* row_token;
+    int2* list;
     int32_t E, nblk, rows_per_block;
+    int32_t blocks_per_window, groups_per_window;
 };
 
-// Rows of the items. Every workgroup first turns the E expert totals into expert offsets (an
-// exclusive scan in LDS: E <= 1024 is four values a thread); workgroup 0 also writes the count
-// outputs. Item i of block b with expert e then takes row
-// expert_offset[e] + prefix[e * nblk + b] + local_rank[i], recorded in token_row[i] and
-// row_token[row]; an id outside [0, E) gets token_row -1 and no row. LDS: eoff [E + 1] u32.
+// Rows of the items. Workgroup g of window w takes kThreads items of the window. Every workgroup
+// first turns the E expert totals into expert offsets (an exclusive scan in LDS: E <= 1024 is four
+// values a thread) and the window's per-expert row counts
+// n[e] = prefix[e * nblk + b1] - prefix[e * nblk + b0] into their exclusive scan C[e] (rows of
+// lower experts in the window); workgroup 0 also writes the count outputs. Item i of block b with
+// expert e then takes row expert_offset[e] + prefix[e * nblk + b] + local_rank[i] (recorded in
+// token_row[i] and row_token[row]) and list position C[e] + prefix[e * nblk + b] -
+// prefix[e * nblk + b0] + local_rank[i] within its window. An id outside [0, E) gets token_row -1
+// and no row. LDS: eoff [E + 1] u32, qbase [E] i32.
 __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R, int32_t k,
                                                           CountOutputs co)
 {
     constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
     __shared__ uint32_t eoff[MOE_MAX_EXPERTS + 1];
+    __shared__ int32_t qbase[MOE_MAX_EXPERTS];
     __shared__ uint32_t wave_tot[kWaves];
     const int tid = threadIdx.x, E = rp.E;
-    uint32_t v[kPer];
-    uint32_t mine = 0u;
+    const int w = blockIdx.x / rp.groups_per_window;
+    const int g = blockIdx.x - w * rp.groups_per_window;
+    const int b0 = w * rp.blocks_per_window;
+    const int b1 = min(b0 + rp.blocks_per_window, rp.nblk);
+    const bool in_window = b0 < rp.nblk;                 // uniform: false only for an empty batch
+    uint32_t v[kPer], p0[kPer], n[kPer];
+    uint32_t mine = 0u, mine_n = 0u;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         const int e = tid * kPer + u;
-        v[u] = e < E ? rp.totals[e] : 0u;
+        const bool ok = e < E;
+        v[u] = ok ? rp.totals[e] : 0u;
+        p0[u] = (ok && in_window) ? rp.prefix[(int64_t)e * rp.nblk + b0] : 0u;
+        const uint32_t p1 = (ok && in_window)
+                                ? (b1 < rp.nblk ? rp.prefix[(int64_t)e * rp.nblk + b1] : v[u])
+                                : 0u;
+        n[u] = p1 - p0[u];
         mine += v[u];
+        mine_n += n[u];
     }
-    uint32_t total = 0u;
+    uint32_t total = 0u, window_rows = 0u;
     uint32_t run = block_exclusive_scan<kThreads>(mine, wave_tot, &total);
+    __syncthreads();                                     // wave_tot is reused below
+    uint32_t run_n = block_exclusive_scan<kThreads>(mine_n, wave_tot, &window_rows);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         const int e = tid * kPer + u;
-        if (e < E)
+        if (e < E) {
             eoff[e] = run;
+            qbase[e] = (int32_t)(run_n - p0[u]);
+        }
         run += v[u];
+        run_n += n[u];
     }
     if (tid == 0)
         eoff[E] = total;
@@ -488,17 +517,27 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
             co.rank_offsets[co.N] = (int32_t)total;
         }
     }
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < R;
-         i += (int64_t)gridDim.x * kThreads) {
-        const int e = rp.topk_idx[i];
-        int32_t row = -1;
-        if ((uint32_t)e < (uint32_t)E)
-            row = (int32_t)(eoff[e] + rp.prefix[(int64_t)e * rp.nblk + i / rp.rows_per_block] +
-                            rp.local_rank[i]);
-        rp.token_row[i] = row;
-        if ((uint32_t)row < (uint32_t)R)
-            rp.row_token[row] = (int32_t)(i / k);
+    if (!in_window)
+        return;
+    const int64_t w0 = (int64_t)b0 * rp.rows_per_block;
+    const int64_t w1 = min((int64_t)b1 * rp.rows_per_block, (int64_t)R);
+    const int64_t i = w0 + (int64_t)g * kThreads + tid;
+    if (i >= w1)
+        return;
+    const int e = rp.topk_idx[i];
+    const int32_t t = (int32_t)(i / k);
+    int32_t row = -1;
+    if ((uint32_t)e < (uint32_t)E) {
+        const uint32_t pf =
+            rp.prefix[(int64_t)e * rp.nblk + i / rp.rows_per_block] + rp.local_rank[i];
+        row = (int32_t)(eoff[e] + pf);
+        rp.list[w0 + (qbase[e] + (int32_t)pf)] = make_int2(row, t);
     }
+    rp.token_row[i] = row;
+    if ((uint32_t)row < (uint32_t)R)
+        rp.row_token[row] = t;
+    if (i - w0 >= (int64_t)window_rows)                  // past the window's valid rows
+        rp.list[i] = make_int2(-1, -1);
 }
 
 // ----------------------------------------------------------------------------------- packing --
@@ -521,29 +560,83 @@ __device__ __forceinline__ XcdItem xcd_item(int waves_per_group, int items_per_t
     return it;
 }
 
-// One wavefront per (token t, slot j, piece of 64 chunks): lane l copies chunk piece*64 + l
-// (16 bytes) of x's row t to row token_row[t*k + j] with a non-temporal store. The x load (plain:
-// the k*pieces wavefronts of the token share the row through the XCD's L2) is issued before the
-// row is read. Pieces of one row sit in consecutive wavefronts, so a whole row is written at
-// nearly the same time. A row outside [0, R) is skipped.
+// Which row a packing wavefront copies, and from which token. TOKEN_ORDER: wavefront
+// (token t, slot j, piece) with row token_row[t*k + j]; the k*pieces wavefronts of a token run on
+// one XCD (tokens x, x+8, ... on XCD x), so x's row is read from HBM once and then from that
+// L2. WINDOWS: wavefront (window w, list position q, piece) with (row, token) = list[w*rw + q];
+// the windows of XCD x are x, x+8, ..., so the window's x rows stay in one L2 while its rows go
+// out in ascending order, which keeps the writes of the whole GPU in a narrow address range.
+enum PackOrder { PACK_TOKEN_ORDER = 0, PACK_WINDOWS = 1 };
+
+struct PackPlan {
+    const int32_t* token_row;
+    const int2* list;
+    int32_t T, k, R, pieces;
+    int32_t rows_per_window, nwin;
+};
+
+// The (token, row, piece) of a wavefront: for TOKEN_ORDER the row is read by the caller after
+// the x load has been issued (row = -1 here), for WINDOWS both come from the list. token = -1:
+// nothing to copy.
+struct PackItem {
+    int64_t token;
+    int64_t index;       // TOKEN_ORDER: t*k + j (where token_row holds the row)
+    int32_t row;
+    int piece;
+};
+
+template <int ORDER>
+__device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
+{
+    PackItem it;
+    it.token = -1;
+    it.index = 0;
+    it.row = -1;
+    it.piece = 0;
+    if constexpr (ORDER == PACK_TOKEN_ORDER) {
+        const XcdItem xi = xcd_item(kPackWaves, pp.k * pp.pieces);
+        if (xi.token < pp.T) {
+            const int j = xi.sub / pp.pieces;
+            it.piece = xi.sub - j * pp.pieces;
+            it.index = xi.token * pp.k + j;
+            it.token = xi.token;
+        }
+    } else {
+        const XcdItem xi = xcd_item(kPackWaves, pp.rows_per_window * pp.pieces);
+        const int q = xi.sub / pp.pieces;
+        const int64_t pos = xi.token * pp.rows_per_window + q;   // "token" is the window here
+        if (xi.token < pp.nwin && pos < pp.R) {
+            it.piece = xi.sub - q * pp.pieces;
+            const int2 rt = pp.list[pos];
+            if ((uint32_t)rt.x < (uint32_t)pp.R) {
+                it.row = rt.x;
+                it.token = rt.y;
+            }
+        }
+    }
+    return it;
+}
+
+// One wavefront per (row, 1 KB piece of it): lane l copies chunk piece*64 + l (16 bytes) of x's
+// row to the destination row with a non-temporal store; x is read with plain loads so the
+// wavefronts that copy the same token find it in L2. The pieces of a row run side by side. A row
+// outside [0, R) is skipped.
+template <int ORDER>
 __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows(const u32x4* __restrict__ x,
-                                                               int32_t T, int32_t k, int32_t R,
                                                                int32_t chunks_per_row,
-                                                               int32_t pieces,
-                                                               const int32_t* __restrict__ token_row,
+                                                               PackPlan pp,
                                                                u32x4* __restrict__ recv)
 {
-    const XcdItem it = xcd_item(kPackWaves, k * pieces);
-    if (it.token >= T)
-        return;
-    const int j = it.sub / pieces, piece = it.sub - j * pieces;
-    const int c = piece * 64 + (threadIdx.x & 63);
+    const PackItem it = pack_item<ORDER>(pp);
+    if (it.token < 0)
+        return;                                          // uniform per wavefront
+    const int c = it.piece * 64 + (threadIdx.x & 63);
     const bool active = c < chunks_per_row;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (active)
         v = x[it.token * chunks_per_row + c];
-    const int32_t row = token_row[it.token * k + j];
-    if (active && (uint32_t)row < (uint32_t)R)
+    const int32_t row = ORDER == PACK_TOKEN_ORDER ? pp.token_row[it.index] : it.row;
+    if (active && (uint32_t)row < (uint32_t)pp.R)
         __builtin_nontemporal_store(v, recv + (int64_t)row * chunks_per_row + c);
 }
 
@@ -578,23 +671,21 @@ struct Load8<uint16_t> {
     }
 };
 
-// fp8 packing, one wavefront per (token t, slot j, piece of 64 chunks of 8 elements). The 16
-// lanes of a DPP row hold the 128 elements of one scale block (H % 128 == 0, so a row of lanes is
-// all active or all inactive); every lane takes part in the reduction, only the stores are
-// masked. Scale s = amax / 448 (1 for an all-zero block), codes e4m3(x / s). The row is read
-// after the block has been quantised.
-template <typename XT>
+// fp8 packing, one wavefront per (row, piece of 64 chunks of 8 elements), placed as in
+// k_pack_rows (in token order the row is read after the block has been quantised). The 16 lanes
+// of a DPP row hold the 128 elements of one scale block (H % 128 == 0, so a row of lanes is all
+// active or all inactive); every lane takes part in the reduction, only the stores are masked.
+// Scale s = amax / 448 (1 for an all-zero block), codes e4m3(x / s).
+template <typename XT, int ORDER>
 __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
-    const XT* __restrict__ x, int32_t T, int32_t H, int32_t k, int32_t R, int32_t pieces,
-    const int32_t* __restrict__ token_row, uint8_t* __restrict__ recv,
+    const XT* __restrict__ x, int32_t H, PackPlan pp, uint8_t* __restrict__ recv,
     float* __restrict__ recv_scales)
 {
-    const XcdItem it = xcd_item(kPackWaves, k * pieces);
-    if (it.token >= T)
-        return;
-    const int j = it.sub / pieces, piece = it.sub - j * pieces;
+    const PackItem it = pack_item<ORDER>(pp);
+    if (it.token < 0)
+        return;                                          // uniform per wavefront
     const int lane = threadIdx.x & 63;
-    const int c = piece * 64 + lane;
+    const int c = it.piece * 64 + lane;
     const bool active = c < H / 8;
     float v[8];
     if (active) {
@@ -617,8 +708,8 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
     u32x2 packed;
     packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
     packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-    const int32_t row = token_row[it.token * k + j];
-    if (!active || (uint32_t)row >= (uint32_t)R)
+    const int32_t row = ORDER == PACK_TOKEN_ORDER ? pp.token_row[it.index] : it.row;
+    if (!active || (uint32_t)row >= (uint32_t)pp.R)
         return;
     __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(recv + (int64_t)row * H) + c);
     if ((lane & 15) == 0)
@@ -789,13 +880,15 @@ inline size_t hist_lds_bytes(int32_t E)
     return (size_t)kWaves * E * sizeof(uint64_t) + (size_t)E * sizeof(uint32_t);
 }
 
-// Workspace: expert-major histograms [E * nblk], per-block prefixes [E * nblk], expert totals
-// [E], in-block ranks [R]; each piece 256-byte aligned; nblk covers both layout plans.
+// Workspace: block-major histograms [nblk * E], expert-major prefixes [E * nblk], expert totals
+// [E], in-block ranks [R], the windows' (row, token) lists [R]; each piece 256-byte aligned; nblk
+// covers both layout plans.
 struct Workspace {
-    uint32_t* hist_t;
+    uint32_t* hist;
     uint32_t* prefix;
     uint32_t* totals;
     uint32_t* local_rank;
+    int2* list;
 };
 
 inline int64_t ws_nblk(int32_t T, int32_t k)
@@ -814,8 +907,9 @@ inline size_t ws_hist_bytes(int32_t T, int32_t E, int32_t k)
 inline size_t ws_bytes(int32_t T, int32_t E, int32_t k)
 {
     const int64_t R = (int64_t)T * k;
+    const size_t rr = (size_t)(R > 0 ? R : 1);
     return 2 * ws_hist_bytes(T, E, k) + align_up((size_t)E * sizeof(uint32_t), 256) +
-           align_up((size_t)(R > 0 ? R : 1) * sizeof(uint32_t), 256);
+           align_up(rr * sizeof(uint32_t), 256) + align_up(rr * sizeof(int2), 256);
 }
 
 inline Workspace carve_workspace(void* base, int32_t T, int32_t E, int32_t k)
@@ -824,11 +918,44 @@ inline Workspace carve_workspace(void* base, int32_t T, int32_t E, int32_t k)
     const size_t hb = ws_hist_bytes(T, E, k);
     const size_t tb = align_up((size_t)E * sizeof(uint32_t), 256);
     Workspace w;
-    w.hist_t = reinterpret_cast<uint32_t*>(p);
+    w.hist = reinterpret_cast<uint32_t*>(p);
     w.prefix = reinterpret_cast<uint32_t*>(p + hb);
     w.totals = reinterpret_cast<uint32_t*>(p + 2 * hb);
     w.local_rank = reinterpret_cast<uint32_t*>(p + 2 * hb + tb);
+    const int64_t R = (int64_t)T * k;
+    w.list = reinterpret_cast<int2*>(p + 2 * hb + tb +
+                                     align_up((size_t)(R > 0 ? R : 1) * sizeof(uint32_t), 256));
     return w;
+}
+
+// Packing windows: about as many layout blocks as keep the window's x rows within kWindowBytes
+// (they stay in one XCD's L2 while the window is packed, with room to spare for what earlier
+// kernels left there), with the window count rounded up to a multiple of 8 so that every XCD gets
+// the same number of windows. x_row_bytes = 0 (no packing follows) takes 8 windows.
+constexpr int64_t kWindowBytes = 1792 * 1024;
+
+struct WindowPlan {
+    int32_t blocks_per_window;
+    int32_t rows_per_window;
+    int32_t nwin;
+};
+
+inline WindowPlan window_plan(const LayoutPlan& lp, int64_t x_row_bytes, int32_t k)
+{
+    int64_t fit = lp.nblk;
+    if (x_row_bytes > 0) {
+        const int64_t tokens = kWindowBytes / x_row_bytes > 1 ? kWindowBytes / x_row_bytes : 1;
+        fit = tokens * k / lp.rows_per_block;
+        if (fit < 1)
+            fit = 1;
+    }
+    const int64_t nwin_target = kXcds * (lp.nblk > 0 ? ceil_div(lp.nblk, kXcds * fit) : 1);
+    const int64_t bpw = lp.nblk > 0 ? ceil_div(lp.nblk, nwin_target) : 1;
+    WindowPlan wp;
+    wp.blocks_per_window = (int32_t)bpw;
+    wp.rows_per_window = (int32_t)(bpw * lp.rows_per_block);
+    wp.nwin = (int32_t)ceil_div(lp.nblk, bpw);
+    return wp;
 }
 
 inline int64_t xcd_blocks(int32_t T, int64_t items_per_token, int waves_per_group)
@@ -926,8 +1053,8 @@ void launch_route_layout(const float* logits, int32_t T, int32_t E, int32_t k,
 {
     const dim3 grid((unsigned)plan.nblk);
     const size_t lds = (size_t)E * sizeof(uint32_t);
-    MOE_ROUTE_LAUNCH(k_route_layout, grid, kGroupThreads, lds, logits, T, E, k, plan.nblk,
-                     topk_idx, topk_w, ws.hist_t, ws.local_rank);
+    MOE_ROUTE_LAUNCH(k_route_layout, grid, kGroupThreads, lds, logits, T, E, k, topk_idx, topk_w,
+                     ws.hist, ws.local_rank);
 }
 
 void launch_hist(const int32_t* topk_idx, int64_t R, int32_t E, const Workspace& ws,
@@ -935,7 +1062,7 @@ void launch_hist(const int32_t* topk_idx, int64_t R, int32_t E, const Workspace&
 {
     if (plan.nblk > 0)
         k_layout_hist<<<plan.nblk, kThreads, hist_lds_bytes(E), stream>>>(
-            topk_idx, (int32_t)R, E, plan.rows_per_block, plan.nblk, ws.hist_t, ws.local_rank);
+            topk_idx, (int32_t)R, E, plan.rows_per_block, ws.hist, ws.local_rank);
 }
 
 CountOutputs count_outputs(const moe_dispatch_out_t* out, int32_t n_ranks)
@@ -953,12 +1080,12 @@ CountOutputs count_outputs(const moe_dispatch_out_t* out, int32_t n_ranks)
 // runs even for an empty batch).
 void launch_scan_rows(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E,
                       const moe_dispatch_out_t* out, int32_t n_ranks, const Workspace& ws,
-                      const LayoutPlan& plan, hipStream_t stream)
+                      const LayoutPlan& plan, const WindowPlan& wp, hipStream_t stream)
 {
     const dim3 grid((unsigned)ceil_div(E, kGroupWaves));
     const int64_t s = ceil_div(plan.nblk, 64);
 #define MOE_SCAN(SS)                                                                              \
-    k_expert_scan<SS><<<grid, kGroupThreads, 0, stream>>>(ws.hist_t, E, plan.nblk, ws.prefix,    \
+    k_expert_scan<SS><<<grid, kGroupThreads, 0, stream>>>(ws.hist, E, plan.nblk, ws.prefix,      \
                                                           ws.totals)
     if (s <= 1)
         MOE_SCAN(1);
@@ -981,37 +1108,63 @@ void launch_scan_rows(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E,
     rp.E = E;
     rp.nblk = plan.nblk;
     rp.rows_per_block = plan.rows_per_block;
-    const int64_t want = ceil_div(R, kThreads);
-    const unsigned blocks = (unsigned)(want < 1 ? 1 : want < 4096 ? want : 4096);
-    k_layout_rows<<<blocks, kThreads, 0, stream>>>(rp, R, k, count_outputs(out, n_ranks));
+    rp.list = ws.list;
+    rp.blocks_per_window = wp.blocks_per_window;
+    rp.groups_per_window = (int32_t)ceil_div(wp.rows_per_window, kThreads);
+    const int64_t want = (int64_t)wp.nwin * rp.groups_per_window;
+    k_layout_rows<<<(unsigned)(want < 1 ? 1 : want), kThreads, 0, stream>>>(
+        rp, R, k, count_outputs(out, n_ranks));
 }
 
+// Packing in token order (token_row given), or by windows from the list the rows kernel wrote.
 void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t k,
-                 const int32_t* token_row, moe_dtype_t payload_dtype, void* recv,
-                 float* recv_scales, hipStream_t stream)
+                 const int32_t* token_row, const int2* list, const WindowPlan* wp,
+                 moe_dtype_t payload_dtype, void* recv, float* recv_scales, hipStream_t stream)
 {
     const int32_t R = T * k;
     if (R == 0)
         return;
-    if (payload_dtype != MOE_FP8_E4M3) {
-        const int32_t cpr = (int32_t)((int64_t)H * (int64_t)dtype_size(x_dtype) / 16);
-        const int32_t pieces = (int32_t)ceil_div(cpr, 64);
-        const dim3 grid((unsigned)xcd_blocks(T, (int64_t)k * pieces, kPackWaves));
-        k_pack_rows<<<grid, 64 * kPackWaves, 0, stream>>>(static_cast<const u32x4*>(x), T, k, R,
-                                                          cpr, pieces, token_row,
-                                                          static_cast<u32x4*>(recv));
-    } else {
-        const int32_t pieces = (int32_t)ceil_div(H / 8, 64);
-        const dim3 grid((unsigned)xcd_blocks(T, (int64_t)k * pieces, kPackWaves));
-        if (x_dtype == MOE_F32)
-            k_pack_rows_fp8<float><<<grid, 64 * kPackWaves, 0, stream>>>(
-                static_cast<const float*>(x), T, H, k, R, pieces, token_row,
-                static_cast<uint8_t*>(recv), recv_scales);
+    const bool fp8 = payload_dtype == MOE_FP8_E4M3;
+    const int32_t cpr = (int32_t)((int64_t)H * (int64_t)dtype_size(x_dtype) / 16);
+    PackPlan pp;
+    pp.token_row = token_row;
+    pp.list = list;
+    pp.T = T;
+    pp.k = k;
+    pp.R = R;
+    pp.pieces = (int32_t)ceil_div(fp8 ? H / 8 : cpr, 64);
+    pp.rows_per_window = wp ? wp->rows_per_window : 0;
+    pp.nwin = wp ? wp->nwin : 0;
+    const bool windows = wp && (int64_t)pp.rows_per_window * pp.pieces < (int64_t)INT32_MAX / 2;
+    const dim3 grid((unsigned)(windows ? xcd_blocks(pp.nwin, (int64_t)pp.rows_per_window *
+                                                                 pp.pieces, kPackWaves)
+                                       : xcd_blocks(T, (int64_t)k * pp.pieces, kPackWaves)));
+    const dim3 block(64 * kPackWaves);
+    const u32x4* xs = static_cast<const u32x4*>(x);
+    if (!fp8) {
+        u32x4* rv = static_cast<u32x4*>(recv);
+        if (windows)
+            k_pack_rows<PACK_WINDOWS><<<grid, block, 0, stream>>>(xs, cpr, pp, rv);
         else
-            k_pack_rows_fp8<uint16_t><<<grid, 64 * kPackWaves, 0, stream>>>(
-                static_cast<const uint16_t*>(x), T, H, k, R, pieces, token_row,
-                static_cast<uint8_t*>(recv), recv_scales);
+            k_pack_rows<PACK_TOKEN_ORDER><<<grid, block, 0, stream>>>(xs, cpr, pp, rv);
+        return;
     }
+    uint8_t* rv = static_cast<uint8_t*>(recv);
+#define MOE_PACK_FP8(XT, ORD)                                                                     \
+    k_pack_rows_fp8<XT, ORD><<<grid, block, 0, stream>>>(static_cast<const XT*>(x), H, pp, rv,    \
+                                                         recv_scales)
+    if (x_dtype == MOE_F32) {
+        if (windows)
+            MOE_PACK_FP8(float, PACK_WINDOWS);
+        else
+            MOE_PACK_FP8(float, PACK_TOKEN_ORDER);
+    } else {
+        if (windows)
+            MOE_PACK_FP8(uint16_t, PACK_WINDOWS);
+        else
+            MOE_PACK_FP8(uint16_t, PACK_TOKEN_ORDER);
+    }
+#undef MOE_PACK_FP8
 }
 
 template <typename YT, typename OT>
@@ -1089,7 +1242,8 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, 
     const LayoutPlan plan = hist_plan(R);
     const Workspace ws = carve_workspace(workspace, T, E, k);
     launch_hist(topk_idx, R, E, ws, plan, stream);
-    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, stream);
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, window_plan(plan, 0, k),
+                     stream);
     return launch_status();
 }
 
@@ -1103,7 +1257,8 @@ moe_status_t moe_dispatch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, in
         return st;
     if (T == 0)
         return MOE_OK;
-    launch_pack(x, x_dtype, T, H, k, token_row, payload_dtype, recv, recv_scales, stream);
+    launch_pack(x, x_dtype, T, H, k, token_row, nullptr, nullptr, payload_dtype, recv,
+                recv_scales, stream);
     return launch_status();
 }
 
@@ -1127,9 +1282,10 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
     const LayoutPlan plan = hist_plan(R);
     const Workspace ws = carve_workspace(workspace, T, E, k);
     launch_hist(topk_idx, R, E, ws, plan, stream);
-    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, stream);
-    launch_pack(x, x_dtype, T, H, k, out->token_row, payload_dtype, out->recv, out->recv_scales,
-                stream);
+    const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, wp, stream);
+    launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
+                out->recv_scales, stream);
     return launch_status();
 }
 
@@ -1165,9 +1321,10 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
             launch_route(logits, T, E, k, topk_idx, topk_w, stream);
         launch_hist(topk_idx, R, E, ws, plan, stream);
     }
-    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, stream);
-    launch_pack(x, x_dtype, T, H, k, out->token_row, payload_dtype, out->recv, out->recv_scales,
-                stream);
+    const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, wp, stream);
+    launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
+                out->recv_scales, stream);
     return launch_status();
 }
 

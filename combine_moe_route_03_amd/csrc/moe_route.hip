@@ -15,6 +15,8 @@
 //                    (token, slot) from one LDS bit mask per expert;
 //   k_layout_hist    for caller-given expert ids: per block of items, stable in-block ranks from
 //                    per-wavefront LDS bit masks, and the block's expert histogram;
+//   k_route_layout_small  for small batches: routing, counting, offsets and row maps in one
+//                    workgroup, entirely in LDS;
 //   k_expert_scan    one wavefront per expert scans its blocks' counts into per-block prefixes
 //                    and the expert's total (many workgroups);
 //   k_layout_rows    every workgroup scans the expert totals into offsets in LDS, then writes
@@ -39,6 +41,8 @@ constexpr int kGroupThreads = 1024;      // 16-wavefront workgroups (route-layou
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kRouteTokens = kGroupWaves;   // tokens per route-layout workgroup (one per wave)
 constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
+constexpr int kSmallTokens = 32;         // small batches: routing and layout in one workgroup
+constexpr int kSmallItems = 2048;        //   (T <= 32 tokens, at most 2 per wavefront)
 constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
 constexpr int kCombineWaves = 2;         // wavefronts per combine workgroup
 constexpr int kXcds = 8;                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
@@ -212,24 +216,36 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// The logits of one token, lane l holding experts l, l+64, ... (entries past E are not read).
+template <int PL>
+__device__ __forceinline__ void load_logits(const float* __restrict__ l, int32_t E, float (&v)[PL])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int p = 0; p < PL; ++p) {
+        const int e = lane + 64 * p;
+        v[p] = (e < E) ? l[e] : 0.0f;
+    }
+}
+
 // Top-k of one token by one whole wavefront (all lanes active). Lane l holds experts l, l+64, ...
 // (coalesced loads) and sorts its keys once, largest first, so its best remaining candidate is
 // always key[0]. Each of the k rounds takes the wave-wide maximum of the candidates' logit words;
 // when a single lane holds it (the usual case, found with one ballot) that lane wins, otherwise the
 // lowest expert id among the tied lanes wins. The winner drops its head. The weights use
 // double-precision exp and division, rounded once to fp32. Lane j < k writes slot j and returns
-// its expert id (other lanes return -1).
+// its expert id (other lanes return -1). The logits come from load_logits.
 template <int PL>
-__device__ __forceinline__ int route_token(const float* __restrict__ l, int32_t E, int32_t k,
-                                           int32_t* __restrict__ idx_out,
-                                           float* __restrict__ w_out)
+__device__ __forceinline__ int route_token_from(const float (&v)[PL], int32_t E, int32_t k,
+                                                int32_t* __restrict__ idx_out,
+                                                float* __restrict__ w_out)
 {
     const int lane = threadIdx.x & 63;
     uint64_t key[PL];
 #pragma unroll
     for (int p = 0; p < PL; ++p) {
         const int e = lane + 64 * p;
-        key[p] = (e < E) ? route_key(l[e], e) : 0ull;
+        key[p] = (e < E) ? route_key(v[p], e) : 0ull;
     }
 #pragma unroll
     for (int r = 0; r < PL; ++r)                        // odd-even transposition sort, descending
@@ -275,6 +291,16 @@ __device__ __forceinline__ int route_token(const float* __restrict__ l, int32_t 
         w_out[lane] = (float)(ex / sum);
     }
     return my_id;
+}
+
+template <int PL>
+__device__ __forceinline__ int route_token(const float* __restrict__ l, int32_t E, int32_t k,
+                                           int32_t* __restrict__ idx_out,
+                                           float* __restrict__ w_out)
+{
+    float v[PL];
+    load_logits<PL>(l, E, v);
+    return route_token_from<PL>(v, E, k, idx_out, w_out);
 }
 
 template <int PL>
@@ -540,6 +566,100 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
         rp.list[i] = make_int2(-1, -1);
 }
 
+// Routing and the whole layout of a small batch (T <= kSmallTokens, T*k <= kSmallItems) in one
+// workgroup of 16 wavefronts, with no step between workgroups. Wavefront w routes tokens w, w+16,
+// ... (loading the next token's logits before routing the current one); the expert ids stay in LDS
+// and LDS counters count the experts. One block scan gives the expert offsets and the count
+// outputs. Then the tokens are taken 16 at a time, in order: token 16c + w sets bit w in the LDS
+// masks of its experts, and item (t, j) with expert e takes row
+// eoff[e] + run[e] + popcount(mask[e] & bits below w); run[e] then advances by popcount(mask[e]).
+// Routed ids are distinct within a token, so this is the stable (expert, token, slot) order.
+// LDS: ids [kSmallItems] u16, count/run [E], offsets [E + 1], masks [E] u32.
+template <int PL>
+__global__ __launch_bounds__(kGroupThreads) void k_route_layout_small(
+    const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ token_row,
+    int32_t* __restrict__ row_token, CountOutputs co)
+{
+    __shared__ uint16_t ids[kSmallItems];
+    __shared__ uint32_t run[MOE_MAX_EXPERTS];
+    __shared__ uint32_t eoff[MOE_MAX_EXPERTS + 1];
+    __shared__ uint32_t mask[MOE_MAX_EXPERTS];
+    __shared__ uint32_t wave_tot[kGroupWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += kGroupThreads) {
+        run[e] = 0u;
+        mask[e] = 0u;
+    }
+    __syncthreads();
+    float cur[PL], nxt[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p)
+        nxt[p] = 0.0f;
+    if (wave < T)
+        load_logits<PL>(logits + (int64_t)wave * E, E, cur);
+    for (int t = wave; t < T; t += kGroupWaves) {       // uniform per wavefront
+        const int tn = t + kGroupWaves;
+        if (tn < T)
+            load_logits<PL>(logits + (int64_t)tn * E, E, nxt);
+        const int id = route_token_from<PL>(cur, E, k, topk_idx + (int64_t)t * k,
+                                            topk_w + (int64_t)t * k);
+        if (id >= 0) {
+            ids[t * k + lane] = (uint16_t)id;
+            atomicAdd(&run[id], 1u);
+        }
+#pragma unroll
+        for (int p = 0; p < PL; ++p)
+            cur[p] = nxt[p];
+    }
+    __syncthreads();
+    const uint32_t mine = tid < E ? run[tid] : 0u;    // E <= 1024: one expert per thread
+    uint32_t total = 0u;
+    const uint32_t ex = block_exclusive_scan<kGroupThreads>(mine, wave_tot, &total);
+    if (tid < E) {
+        eoff[tid] = ex;
+        run[tid] = 0u;
+    }
+    if (tid == 0)
+        eoff[E] = total;
+    __syncthreads();
+    const int epr = E / co.N;
+    if (tid < E) {
+        co.expert_offsets[tid] = (int32_t)eoff[tid];
+        co.expert_counts[tid] = (int32_t)(eoff[tid + 1] - eoff[tid]);
+    }
+    for (int r = tid; r < co.N; r += kGroupThreads) {
+        co.rank_offsets[r] = (int32_t)eoff[r * epr];
+        co.rank_counts[r] = (int32_t)(eoff[(r + 1) * epr] - eoff[r * epr]);
+    }
+    if (tid == 0) {
+        co.expert_offsets[E] = (int32_t)total;
+        co.rank_offsets[co.N] = (int32_t)total;
+    }
+    for (int c0 = 0; c0 < T; c0 += kGroupWaves) {      // uniform across the workgroup
+        const int t = c0 + wave;
+        const bool mine_item = t < T && lane < k;
+        const int e = mine_item ? (int)ids[t * k + lane] : 0;
+        if (mine_item)
+            atomicOr(&mask[e], 1u << wave);
+        __syncthreads();
+        if (mine_item) {
+            const uint32_t row = eoff[e] + run[e] + (uint32_t)__popc(mask[e] & ((1u << wave) - 1u));
+            token_row[t * k + lane] = (int32_t)row;
+            row_token[row] = t;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kGroupThreads) {
+            const uint32_t m = mask[ee];
+            if (m != 0u) {
+                run[ee] += (uint32_t)__popc(m);
+                mask[ee] = 0u;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ----------------------------------------------------------------------------------- packing --
 // Wavefront placement of the row kernels. Wavefront w of workgroup blk handles item
 // m = (blk / 8) * waves_per_group + w of XCD blk % 8. Items of XCD x belong to tokens
@@ -671,30 +791,33 @@ struct Load8<uint16_t> {
     }
 };
 
-// fp8 packing, one wavefront per (row, piece of 64 chunks of 8 elements), placed as in
-// k_pack_rows (in token order the row is read after the block has been quantised). The 16 lanes
-// of a DPP row hold the 128 elements of one scale block (H % 128 == 0, so a row of lanes is all
-// active or all inactive); every lane takes part in the reduction, only the stores are masked.
-// Scale s = amax / 448 (1 for an all-zero block), codes e4m3(x / s).
-template <typename XT, int ORDER>
+// fp8 packing, one wavefront per (token t, piece of 64 chunks of 8 elements), placed like the
+// token-order packing (tokens x, x+8, ... on XCD x). The 16 lanes of a DPP row hold the 128
+// elements of one scale block (H % 128 == 0, so a row of lanes is all active or all inactive);
+// every lane takes part in the reduction, only the stores are masked. Scale s = amax / 448 (1 for
+// an all-zero block), codes e4m3(x / s). Each block is quantised once and its codes and scale are
+// stored to all k rows of the token: lanes j < k read the k rows with one load, and store round j
+// takes row j by readlane. A row outside [0, R) is skipped.
+template <typename XT>
 __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
     const XT* __restrict__ x, int32_t H, PackPlan pp, uint8_t* __restrict__ recv,
     float* __restrict__ recv_scales)
 {
-    const PackItem it = pack_item<ORDER>(pp);
-    if (it.token < 0)
+    const XcdItem xi = xcd_item(kPackWaves, pp.pieces);
+    if (xi.token >= pp.T)
         return;                                          // uniform per wavefront
     const int lane = threadIdx.x & 63;
-    const int c = it.piece * 64 + lane;
+    const int c = xi.sub * 64 + lane;
     const bool active = c < H / 8;
     float v[8];
     if (active) {
-        Load8<XT>::run(x + it.token * H + (int64_t)c * 8, v);
+        Load8<XT>::run(x + xi.token * H + (int64_t)c * 8, v);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             v[i] = 0.0f;
     }
+    const int32_t my_row = lane < pp.k ? pp.token_row[xi.token * pp.k + lane] : -1;
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -708,12 +831,17 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
     u32x2 packed;
     packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
     packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-    const int32_t row = ORDER == PACK_TOKEN_ORDER ? pp.token_row[it.index] : it.row;
-    if (!active || (uint32_t)row >= (uint32_t)pp.R)
-        return;
-    __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(recv + (int64_t)row * H) + c);
-    if ((lane & 15) == 0)
-        recv_scales[(int64_t)row * (H / 128) + c / 16] = s;
+    for (int j = 0; j < pp.k; ++j) {
+        const int32_t row = __builtin_amdgcn_readlane(my_row, j);
+        if ((uint32_t)row >= (uint32_t)pp.R)
+            continue;                                    // uniform per wavefront
+        if (active) {
+            __builtin_nontemporal_store(packed,
+                                        reinterpret_cast<u32x2*>(recv + (int64_t)row * H) + c);
+            if ((lane & 15) == 0)
+                recv_scales[(int64_t)row * (H / 128) + c / 16] = s;
+        }
+    }
 }
 
 // ----------------------------------------------------------------------------------- combine --
@@ -1149,22 +1277,15 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
             k_pack_rows<PACK_TOKEN_ORDER><<<grid, block, 0, stream>>>(xs, cpr, pp, rv);
         return;
     }
+    // fp8: one wavefront per (token, piece), quantised once and stored to the token's k rows
+    const dim3 grid8((unsigned)xcd_blocks(T, pp.pieces, kPackWaves));
     uint8_t* rv = static_cast<uint8_t*>(recv);
-#define MOE_PACK_FP8(XT, ORD)                                                                     \
-    k_pack_rows_fp8<XT, ORD><<<grid, block, 0, stream>>>(static_cast<const XT*>(x), H, pp, rv,    \
-                                                         recv_scales)
-    if (x_dtype == MOE_F32) {
-        if (windows)
-            MOE_PACK_FP8(float, PACK_WINDOWS);
-        else
-            MOE_PACK_FP8(float, PACK_TOKEN_ORDER);
-    } else {
-        if (windows)
-            MOE_PACK_FP8(uint16_t, PACK_WINDOWS);
-        else
-            MOE_PACK_FP8(uint16_t, PACK_TOKEN_ORDER);
-    }
-#undef MOE_PACK_FP8
+    if (x_dtype == MOE_F32)
+        k_pack_rows_fp8<float><<<grid8, block, 0, stream>>>(static_cast<const float*>(x), H, pp,
+                                                            rv, recv_scales);
+    else
+        k_pack_rows_fp8<uint16_t><<<grid8, block, 0, stream>>>(static_cast<const uint16_t*>(x), H,
+                                                               pp, rv, recv_scales);
 }
 
 template <typename YT, typename OT>
@@ -1310,6 +1431,15 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)T * k;
+    if (T > 0 && T <= kSmallTokens && R <= kSmallItems) {
+        // small batch: routing and layout in one workgroup, then the token-order packing
+        MOE_ROUTE_LAUNCH(k_route_layout_small, dim3(1), kGroupThreads, 0, logits, T, E, k,
+                         topk_idx, topk_w, out->token_row, out->row_token,
+                         count_outputs(out, n_ranks));
+        launch_pack(x, x_dtype, T, H, k, out->token_row, nullptr, nullptr, payload_dtype,
+                    out->recv, out->recv_scales, stream);
+        return launch_status();
+    }
     const Workspace ws = carve_workspace(workspace, T, E, k);
     LayoutPlan plan;
     if (T > 0 && fused_route_fits(T)) {

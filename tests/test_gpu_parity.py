@@ -158,6 +158,7 @@ EDGE = [
     (4500, 512, 256, 8, 16, "bf16", "bf16"),    # T*k = 36000: several rows per layout block
     (9000, 256, 1024, 8, 64, "bf16", "bf16"),   # E at its maximum; T*k = 72000 > 64 * 1024
     (3, 128, 1024, 64, 1024, "bf16", "fp8_e4m3"),   # k at its maximum, N = E = 1024
+    (32, 512, 256, 8, 32, "bf16", "fp8_e4m3"),  # most tokens the one-workgroup routing takes
     (16384, 128, 64, 2, 4, "bf16", "bf16"),     # most tokens the fused route-layout takes
     (16401, 128, 64, 2, 4, "f32", "f32"),       # one token more: separate route + histogram
 ]

@@ -60,6 +60,46 @@ WORKLOADS = {
 ORDER = ["tiny", "decode", "decode_fp8", "prefill", "skewed"]
 
 
+@dataclass(frozen=True)
+class EpWorkload:
+    """Expert parallelism over S source devices and N destination ranks, emulated on one GPU."""
+    name: str
+    S: int            # source devices, T tokens each
+    T: int
+    H: int
+    E: int
+    k: int
+    N: int            # destination ranks; rank r hosts experts [r*E/N, (r+1)*E/N)
+    dtype: str        # x, payload, expert output and combine output format
+    seed: int = 0
+
+    @property
+    def L(self) -> int:
+        return self.E // self.N
+
+    @property
+    def cap(self) -> int:
+        """Rows of one (rank, source) region: the most one source can send to one rank."""
+        return self.T * min(self.k, self.L)
+
+    def as_workload(self) -> Workload:
+        """The whole batch (all sources' tokens, source s owning tokens [s*T, (s+1)*T))."""
+        return Workload(self.name, self.S * self.T, self.H, self.E, self.k, self.N, self.dtype,
+                        self.dtype, self.dtype, self.dtype, "identity", seed=self.seed)
+
+
+EP_WORKLOADS = {
+    # 3 sources of 10 tokens, hidden 256 fp32, 8 experts top-2 over 4 ranks of 2 experts.
+    "ep_tiny": EpWorkload("ep_tiny", 3, 10, 256, 8, 2, 4, "f32"),
+    # A decode batch of 128 tokens spread over 8 devices: 16 tokens each, 256 experts top-8 over 8
+    # ranks of 32 experts.
+    "ep_decode": EpWorkload("ep_decode", 8, 16, 7168, 256, 8, 8, "bf16"),
+    # The 4096-token prefill batch spread over 8 devices: 512 tokens each, 384 experts top-8 over
+    # 8 ranks of 48 experts.
+    "ep_prefill": EpWorkload("ep_prefill", 8, 512, 7168, 384, 8, 8, "bf16"),
+}
+
+
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even bf16 bit patterns of an fp32 array (torch's CPU conversion)."""
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)

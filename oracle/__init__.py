@@ -53,6 +53,9 @@ def _load():
             "oracle_dispatch": [P, I, I, I, P, I, I, I, I, P, P, P, P, P, P, P, P],
             "oracle_experts": [P, I, P, I, I, P, I, I, P, I],
             "oracle_combine": [P, I, I, I, I, P, P, P, I],
+            "oracle_ep_send": [P, I, I, I, P, I, I, I, I, I, I, P, P, P],
+            "oracle_ep_recv": [P, I, I, I, I, I, I, I, P, P, P, P, P],
+            "oracle_ep_return": [P, I, I, L, P, P],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -167,3 +170,60 @@ def combine(y, y_dtype: str, token_row, topk_w, out_dtype: str) -> np.ndarray:
     if rc:
         raise ValueError(f"oracle_combine rejected its arguments (code {rc})")
     return out
+
+
+# ------------------------------------------------------------------------------------------------
+# Expert parallelism over S sources and N ranks, emulated on one device: the region array holds
+# one region of `cap` rows per (rank r, source s), at rows [(r*S + s)*cap, (r*S + s + 1)*cap).
+
+def ep_capacity(T: int, E: int, k: int, N: int) -> int:
+    """Rows of one (rank, source) region: the most one source can send to one rank."""
+    return T * min(k, E // N)
+
+
+def ep_send(x, x_dtype: str, topk_idx, E: int, N: int, source: int, S: int, cap: int, regions,
+            region_counts) -> np.ndarray:
+    """Sender half of dispatch for one source: writes its rows into `regions` [N*S*cap, H] and its
+    counts into `region_counts` [N, S, E/N] (both in place); returns send_row int32 [T*k]."""
+    x = _c(x, NP_DTYPES[x_dtype])
+    topk_idx = _c(topk_idx, np.int32)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    assert regions.flags.c_contiguous and regions.shape == (N * S * cap, H)
+    assert region_counts.flags.c_contiguous and region_counts.dtype == np.int32
+    send_row = np.empty(T * k, np.int32)
+    rc = _load().oracle_ep_send(_p(x), DTYPES[x_dtype], T, H, _p(topk_idx), k, E, N, source, S,
+                                cap, _p(regions), _p(region_counts), _p(send_row))
+    if rc:
+        raise ValueError(f"oracle_ep_send rejected its arguments (code {rc})")
+    return send_row
+
+
+def ep_recv(regions, dtype: str, E: int, N: int, rank: int, S: int, cap: int,
+            region_counts) -> dict:
+    """Receiver half of dispatch for one rank: grouped rows [S*cap, H] ordered by (local expert,
+    source, token, slot), per-expert counts and offsets, and each grouped row's region row."""
+    regions = _c(regions, NP_DTYPES[dtype])
+    H = regions.shape[1]
+    L = E // N
+    out = {"grouped": np.zeros((S * cap, H), NP_DTYPES[dtype]),
+           "expert_counts": np.empty(L, np.int32), "expert_offsets": np.empty(L + 1, np.int32),
+           "grouped_src": np.empty(S * cap, np.int32)}
+    rc = _load().oracle_ep_recv(_p(regions), DTYPES[dtype], H, E, N, rank, S, cap,
+                                _p(_c(region_counts, np.int32)), _p(out["grouped"]),
+                                _p(out["expert_counts"]), _p(out["expert_offsets"]),
+                                _p(out["grouped_src"]))
+    if rc:
+        raise ValueError(f"oracle_ep_recv rejected its arguments (code {rc})")
+    return out
+
+
+def ep_return(y_grouped, dtype: str, grouped_src, returns) -> None:
+    """Receiver half of combine: returns[grouped_src[g]] = y_grouped[g] for every valid g."""
+    y_grouped = _c(y_grouped, NP_DTYPES[dtype])
+    assert returns.flags.c_contiguous and returns.dtype == NP_DTYPES[dtype]
+    n, H = y_grouped.shape
+    rc = _load().oracle_ep_return(_p(y_grouped), DTYPES[dtype], H, n,
+                                  _p(_c(grouped_src, np.int32)), _p(returns))
+    if rc:
+        raise ValueError(f"oracle_ep_return rejected its arguments (code {rc})")

@@ -396,3 +396,124 @@ int oracle_combine(const void* y, int32_t y_dtype, int32_t T, int32_t H, int32_t
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Expert parallelism over several devices, emulated on one: S sources (the devices that own the
+ * tokens) and N destination ranks (the devices that host the experts; rank r hosts the L = E/N
+ * experts [r*L, (r+1)*L)). The pages split dispatch and combine into a sender half and a receiver
+ * half ("MoE all-to-all over EFA"), size every receive buffer for the worst case before any row is
+ * written, and let each sender write its rows into the receiver's buffer, after which the receiver
+ * copies them into the input of its grouped GEMM ("Verzend- en ontvangstbuffers", "Dispatch en
+ * Combine"). Readings:
+ *   - the receive buffer of rank r holds one region of `cap` rows per source s, at rows
+ *     [(r*S + s)*cap, (r*S + s + 1)*cap) of one [N*S*cap, H] array; cap >= T*min(k, L), the most
+ *     rows one source can send to one rank (each token at most once per hosted expert);
+ *   - inside its region a source's rows are ordered by (local expert, token, slot), and the
+ *     source publishes region_counts[(r*S + s)*L + l], its rows for expert r*L + l;
+ *   - the receiver's grouped layout is ordered by (local expert, source, token, slot);
+ *   - combine sends every grouped row back to the region row it came from, and the source then
+ *     forms the weighted sum over its token's rows there (the combine above, with the region rows
+ *     as token_row).
+ * ---------------------------------------------------------------------------------------------- */
+
+/* Sender half of dispatch for source `source`: region rows, region counts, and for every (token,
+ * slot) item its row in the region array (send_row[t*k + j]). Payload is x's format. */
+int oracle_ep_send(const void* x, int32_t x_dtype, int32_t T, int32_t H, const int32_t* topk_idx,
+                   int32_t k, int32_t E, int32_t N, int32_t source, int32_t S, int32_t cap,
+                   void* regions, int32_t* region_counts, int32_t* send_row)
+{
+    if (T < 0 || H < 1 || k < 1 || E < 1 || N < 1 || E % N != 0 || S < 1 || source < 0 ||
+        source >= S || x_dtype == ORC_FP8_E4M3)
+        return 1;
+    const int32_t L = E / N;
+    if ((int64_t)cap < (int64_t)T * (k < L ? k : L))
+        return 1;
+    const int64_t R = (int64_t)T * k;
+    for (int64_t i = 0; i < R; i++)
+        if (topk_idx[i] < 0 || topk_idx[i] >= E)
+            return 1;
+    for (int r = 0; r < N; r++)
+        for (int l = 0; l < L; l++)
+            region_counts[((int64_t)r * S + source) * L + l] = 0;
+    for (int64_t i = 0; i < R; i++) {
+        const int e = topk_idx[i];
+        region_counts[((int64_t)(e / L) * S + source) * L + e % L]++;
+    }
+    orc_item_t* items = (orc_item_t*)malloc((size_t)(R > 0 ? R : 1) * sizeof(orc_item_t));
+    if (!items)
+        return 2;
+    for (int64_t t = 0; t < T; t++)
+        for (int j = 0; j < k; j++) {
+            orc_item_t* it = &items[t * k + j];
+            it->expert = topk_idx[t * k + j];
+            it->rank = it->expert / L;
+            it->token = (int32_t)t;
+            it->slot = j;
+        }
+    qsort(items, (size_t)R, sizeof(orc_item_t), item_cmp);
+    const size_t rb = (size_t)H * elem_size(x_dtype);
+    int64_t pos = 0;
+    for (int64_t n = 0; n < R; n++) {
+        if (n > 0 && items[n].rank != items[n - 1].rank)
+            pos = 0;                                   /* a new destination rank: its region */
+        const int64_t row = ((int64_t)items[n].rank * S + source) * cap + pos;
+        pos++;
+        send_row[(int64_t)items[n].token * k + items[n].slot] = (int32_t)row;
+        memcpy((char*)regions + (size_t)row * rb, (const char*)x + (size_t)items[n].token * rb, rb);
+    }
+    free(items);
+    return 0;
+}
+
+/* Receiver half of dispatch for rank `rank`: the grouped layout [S*cap, H] ordered by (local
+ * expert, source, token, slot), its per-expert counts and offsets, and for every grouped row the
+ * region row it was copied from (grouped_src; -1 past the last row). */
+int oracle_ep_recv(const void* regions, int32_t dtype, int32_t H, int32_t E, int32_t N, int32_t rank,
+                   int32_t S, int32_t cap, const int32_t* region_counts, void* grouped,
+                   int32_t* expert_counts, int32_t* expert_offsets, int32_t* grouped_src)
+{
+    if (H < 1 || E < 1 || N < 1 || E % N != 0 || S < 1 || rank < 0 || rank >= N ||
+        dtype == ORC_FP8_E4M3 || cap < 0)
+        return 1;
+    const int32_t L = E / N;
+    const size_t rb = (size_t)H * elem_size(dtype);
+    int64_t g = 0;
+    for (int l = 0; l < L; l++) {
+        expert_offsets[l] = (int32_t)g;
+        for (int s = 0; s < S; s++) {
+            const int32_t* c = region_counts + ((int64_t)rank * S + s) * L;
+            int64_t start = 0;
+            for (int q = 0; q < l; q++)
+                start += c[q];
+            if (start + c[l] > cap)
+                return 1;
+            for (int64_t i = 0; i < c[l]; i++) {
+                const int64_t src = ((int64_t)rank * S + s) * cap + start + i;
+                grouped_src[g] = (int32_t)src;
+                memcpy((char*)grouped + (size_t)g * rb, (const char*)regions + (size_t)src * rb,
+                       rb);
+                g++;
+            }
+        }
+        expert_counts[l] = (int32_t)g - expert_offsets[l];
+    }
+    expert_offsets[L] = (int32_t)g;
+    for (int64_t q = g; q < (int64_t)S * cap; q++)
+        grouped_src[q] = -1;
+    return 0;
+}
+
+/* Receiver half of combine: every grouped row of expert output goes back to the region row it
+ * came from (returns has the layout of the region array). */
+int oracle_ep_return(const void* y_grouped, int32_t dtype, int32_t H, int64_t n_rows,
+                     const int32_t* grouped_src, void* returns)
+{
+    if (H < 1 || dtype == ORC_FP8_E4M3 || n_rows < 0)
+        return 1;
+    const size_t rb = (size_t)H * elem_size(dtype);
+    for (int64_t g = 0; g < n_rows; g++)
+        if (grouped_src[g] >= 0)
+            memcpy((char*)returns + (size_t)grouped_src[g] * rb, (const char*)y_grouped + g * rb,
+                   rb);
+    return 0;
+}

@@ -44,6 +44,15 @@ MUTANTS = {
     "rank_offset_off_by_one": ("rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r];",
                                "rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r] + (r > 0);",
                                "test_oracle_dispatch.py"),
+    "ep_source_major_regions": (
+        "const int64_t row = ((int64_t)items[n].rank * S + source) * cap + pos;",
+        "const int64_t row = ((int64_t)source * N + items[n].rank) * cap + pos;",
+        "test_oracle_ep.py"),
+    "ep_recv_region_start": ("for (int q = 0; q < l; q++)\n                start += c[q];",
+                             "for (int q = 0; q + 1 < l; q++)\n                start += c[q];",
+                             "test_oracle_ep.py"),
+    "ep_return_skips_row_zero": ("if (grouped_src[g] >= 0)", "if (grouped_src[g] > 0)",
+                                 "test_oracle_ep.py"),
 }
 
 

@@ -276,6 +276,95 @@ def other_workloads(torch, moe, dev, names, K):
     return res
 
 
+def ep_emulation(torch, moe, dev, K):
+    """Expert parallelism over S = N = 8 devices emulated on this GPU, at the prefill batch spread
+    512 tokens a device: every source's send, every rank's receive and return, every source's
+    combine. Reports the per-call averages (per device: one of each runs on every device), the
+    whole emulated step and its algorithmic bytes."""
+    import ctypes
+    import numpy as np
+    from combine_moe_route_03_amd.workloads import EP_WORKLOADS, make_inputs
+    w = EP_WORKLOADS["ep_prefill"]
+    lib = moe.load()
+    inp = make_inputs(w.as_workload())
+    S, N, L, cap, T, H, k = w.S, w.N, w.L, w.cap, w.T, w.H, w.k
+    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    idx, wt = moe.moe_route_topk(logits, k)
+    regions = torch.zeros((N * S * cap, H), dtype=torch.bfloat16, device=dev)
+    returns = torch.zeros_like(regions)
+    counts = torch.zeros((N, S, L), dtype=torch.int32, device=dev)
+    rows = [torch.empty(T * k, dtype=torch.int32, device=dev) for _ in range(S)]
+    ws = [moe.alloc_workspace(T, w.E, k, dev) for _ in range(S)]
+    grouped = [torch.zeros((S * cap, H), dtype=torch.bfloat16, device=dev) for _ in range(N)]
+    ec = [torch.empty(L, dtype=torch.int32, device=dev) for _ in range(N)]
+    eo = [torch.empty(L + 1, dtype=torch.int32, device=dev) for _ in range(N)]
+    gs = [torch.empty(S * cap, dtype=torch.int32, device=dev) for _ in range(N)]
+    out = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P, B = ctypes.c_void_p, moe.DTYPE_CODES["bf16"]
+    calls = {"send": [], "recv": [], "return": [], "combine": []}
+    for s in range(S):
+        calls["send"].append(Prepared(
+            lib.moe_ep_send, P(x[s * T:].data_ptr()), B, T, H, P(idx[s * T:].data_ptr()), k, w.E,
+            N, s, S, cap, P(regions.data_ptr()), P(counts.data_ptr()), P(rows[s].data_ptr()),
+            P(ws[s].data_ptr()), ws[s].numel(), stream))
+        calls["combine"].append(Prepared(
+            lib.moe_ep_combine, P(returns.data_ptr()), B, T, H, k, P(rows[s].data_ptr()),
+            P(wt[s * T:].data_ptr()), N * S * cap, P(out[s].data_ptr()), B, stream))
+    for r in range(N):
+        calls["recv"].append(Prepared(
+            lib.moe_ep_recv, P(regions.data_ptr()), B, H, w.E, N, r, S, cap, P(counts.data_ptr()),
+            P(grouped[r].data_ptr()), P(ec[r].data_ptr()), P(eo[r].data_ptr()),
+            P(gs[r].data_ptr()), stream))
+        # expert outputs: the grouped rows themselves (identity experts; the copy is the point)
+        calls["return"].append(Prepared(
+            lib.moe_ep_return, P(grouped[r].data_ptr()), B, H, w.E, N, S, cap,
+            P(gs[r].data_ptr()), P(eo[r].data_ptr()), P(returns.data_ptr()), stream))
+    order = ("send", "recv", "return", "combine")
+
+    def step():
+        for ph in order:
+            for c in calls[ph]:
+                c()
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    tot = {ph: 0.0 for ph in order}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / K
+    for _ in range(K):
+        e[0].record()
+        for p, ph in enumerate(order):
+            for c in calls[ph]:
+                c()
+            e[p + 1].record()
+        torch.cuda.synchronize()
+        for p, ph in enumerate(order):
+            tot[ph] += e[p].elapsed_time(e[p + 1])
+    b = 2
+    rows_total = S * T * k
+    alg = {"send": S * (T * H * b + T * k * H * b + 8 * T * k),
+           "recv": 2 * rows_total * H * b + 4 * rows_total,
+           "return": 2 * rows_total * H * b + 4 * rows_total,
+           "combine": S * (T * k * H * b + 8 * T * k + T * H * b)}
+    per_call = {ph: round(tot[ph] / K / len(calls[ph]) * 1e3, 2) for ph in order}
+    return {"workload": f"{w.name}: {S} sources x {T} tokens, hidden {H} bf16, {w.E} experts "
+                        f"top-{k}, {N} ranks of {L} experts, regions of {cap} rows",
+            "step_us": round(step_ms * 1e3, 1),
+            "per_device_us": round(step_ms * 1e3 / S, 1),
+            "per_call_us": per_call,
+            "phase_GBps": {ph: round(alg[ph] / (tot[ph] / K * 1e-3) / 1e9, 1) for ph in order},
+            "algorithmic_bytes": alg,
+            "GBps": round(sum(alg.values()) / (step_ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -345,7 +434,7 @@ def main():
           ", ".join(f"{ph} {v:.1f} us" for ph, v in split_us.items()) +
           f"; copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
-    others = None
+    others = ep = None
     if args.other_workloads:
         del sets
         torch.cuda.empty_cache()
@@ -354,6 +443,10 @@ def main():
                                  100)
         print("[bench] " + "; ".join(f"{n} {r['us_per_step']} us" for n, r in others.items()),
               file=sys.stderr, flush=True)
+        ep = ep_emulation(torch, moe, dev, 20)
+        torch.cuda.empty_cache()
+        print(f"[bench] expert-parallel emulation: step {ep['step_us']} us, "
+              f"per call {ep['per_call_us']}", file=sys.stderr, flush=True)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -400,6 +493,7 @@ def main():
         "kernel_alone_us": {ph: round(v, 2) for ph, v in kernel_us.items()},
         "copy_ceiling_GBps": round(ceiling["GBps"], 1),
         "other_workloads": others,
+        "ep_emulation": ep,
         "wall_s_timed_loop": round(wall, 4),
         "cpu_baseline": cpu,
     }

@@ -8,7 +8,8 @@ it has not been built.
 _EXPORTS = ("moe_route_topk", "moe_dispatch_workspace_bytes", "moe_dispatch_layout",
             "moe_dispatch_pack", "moe_dispatch", "moe_route_dispatch", "moe_combine",
             "moe_status_str", "alloc_dispatch_out", "alloc_workspace", "DispatchBuffers",
-            "MoeError")
+            "MoeError", "moe_ep_capacity", "moe_ep_send", "moe_ep_recv", "moe_ep_return",
+            "moe_ep_combine")
 
 
 def __getattr__(name):

@@ -57,8 +57,15 @@ def load() -> ctypes.CDLL:
         lib.moe_dispatch.argtypes = [P, I, I, I, P, I, I, I, I, P, P, Z, P]
         lib.moe_route_dispatch.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, Z, P]
         lib.moe_combine.argtypes = [P, I, I, I, I, P, P, P, I, P]
+        lib.moe_ep_capacity.argtypes = [I, I, I, I]
+        lib.moe_ep_capacity.restype = ctypes.c_int64
+        lib.moe_ep_send.argtypes = [P, I, I, I, P, I, I, I, I, I, I, P, P, P, P, Z, P]
+        lib.moe_ep_recv.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P, P, P]
+        lib.moe_ep_return.argtypes = [P, I, I, I, I, I, I, P, P, P, P]
+        lib.moe_ep_combine.argtypes = [P, I, I, I, I, P, P, I, P, I, P]
         for fn in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_dispatch",
-                   "moe_route_dispatch", "moe_combine"):
+                   "moe_route_dispatch", "moe_combine", "moe_ep_send", "moe_ep_recv",
+                   "moe_ep_return", "moe_ep_combine"):
             getattr(lib, fn).restype = I
         _lib = lib
     return _lib
@@ -209,4 +216,58 @@ def moe_combine(y: torch.Tensor, token_row: torch.Tensor, topk_w: torch.Tensor,
     _check("moe_combine", load().moe_combine(
         _ptr(y), _dtype_code(y), T, H, k, _ptr(token_row), _ptr(topk_w), _ptr(out),
         _dtype_code(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# Expert parallelism over S sources and N ranks on one GPU (see include/moe_route.h).
+
+def moe_ep_capacity(T: int, E: int, k: int, n_ranks: int) -> int:
+    return int(load().moe_ep_capacity(T, E, k, n_ranks))
+
+
+def moe_ep_send(x: torch.Tensor, topk_idx: torch.Tensor, E: int, n_ranks: int, source: int,
+                n_sources: int, cap: int, regions: torch.Tensor, region_counts: torch.Tensor,
+                send_row: torch.Tensor, workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Sender half of dispatch for one source; fills its regions, counts and send_row."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    _check("moe_ep_send", load().moe_ep_send(
+        _ptr(x), _dtype_code(x), T, H, _ptr(topk_idx), k, E, n_ranks, source, n_sources, cap,
+        _ptr(regions), _ptr(region_counts), _ptr(send_row), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return send_row
+
+
+def moe_ep_recv(regions: torch.Tensor, E: int, n_ranks: int, rank: int, n_sources: int, cap: int,
+                region_counts: torch.Tensor, grouped: torch.Tensor, expert_counts: torch.Tensor,
+                expert_offsets: torch.Tensor, grouped_src: torch.Tensor, stream=None):
+    """Receiver half of dispatch for one rank: grouped rows, counts, offsets, source rows."""
+    H = regions.shape[1]
+    _check("moe_ep_recv", load().moe_ep_recv(
+        _ptr(regions), _dtype_code(regions), H, E, n_ranks, rank, n_sources, cap,
+        _ptr(region_counts), _ptr(grouped), _ptr(expert_counts), _ptr(expert_offsets),
+        _ptr(grouped_src), _stream(stream)))
+    return grouped
+
+
+def moe_ep_return(y_grouped: torch.Tensor, E: int, n_ranks: int, n_sources: int, cap: int,
+                  grouped_src: torch.Tensor, expert_offsets: torch.Tensor, returns: torch.Tensor,
+                  stream=None) -> torch.Tensor:
+    """Receiver half of combine: expert outputs back to their region rows."""
+    H = y_grouped.shape[1]
+    _check("moe_ep_return", load().moe_ep_return(
+        _ptr(y_grouped), _dtype_code(y_grouped), H, E, n_ranks, n_sources, cap, _ptr(grouped_src),
+        _ptr(expert_offsets), _ptr(returns), _stream(stream)))
+    return returns
+
+
+def moe_ep_combine(returns: torch.Tensor, send_row: torch.Tensor, topk_w: torch.Tensor,
+                   out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Sender half of combine for one source: weighted sum over its returned rows."""
+    T, k = topk_w.shape
+    H = returns.shape[1]
+    _check("moe_ep_combine", load().moe_ep_combine(
+        _ptr(returns), _dtype_code(returns), T, H, k, _ptr(send_row), _ptr(topk_w),
+        returns.shape[0], _ptr(out), _dtype_code(out), _stream(stream)))
     return out

@@ -26,7 +26,11 @@
 //                    16-byte non-temporal store per lane; the pieces of a row run side by side;
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
-//                    fp32 fused multiply-adds, one 16-byte store per 8 outputs.
+//                    fp32 fused multiply-adds, one 16-byte store per 8 outputs;
+//   k_ep_recv_plan   expert-parallel receive: one workgroup turns a rank's per-(source, expert)
+//                    region counts into the grouped layout and each grouped row's region row;
+//   k_copy_rows      grid-stride row gather / scatter by a row map (expert-parallel receive and
+//                    the return half of combine).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -44,6 +48,7 @@ constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront 
 constexpr int kSmallTokens = 32;         // small batches: routing and layout in one workgroup
 constexpr int kSmallItems = 2048;        //   (T <= 32 tokens, at most 2 per wavefront)
 constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
+constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
 constexpr int kCombineWaves = 2;         // wavefronts per combine workgroup
 constexpr int kXcds = 8;                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
 
@@ -462,6 +467,12 @@ struct CountOutputs {
 // x rows of its tokens fit in one XCD's L2. For every window the rows kernel lists the window's
 // (row, token) pairs in ascending row order: list[w0 + q] is the q-th smallest destination row
 // of the window that starts at item w0 (entries past the window's valid rows hold (-1, -1)).
+//
+// Expert-parallel send (ep_counts != nullptr): the rows go to the source's regions instead. Rank
+// r's rows of source s fill region (r, s) = rows [(r*S + s)*cap, ...) in (expert, token, slot)
+// order, so row = (r*S + s)*cap + (expert_offset[e] - expert_offset[r*L]) + prefix + rank (-1
+// past the region's cap rows, which only ids repeated within a token can reach); the
+// per-(rank, source, local expert) counts go to ep_counts, and row_token is not written.
 struct RowPlan {
     const int32_t* topk_idx;
     const uint32_t* local_rank;
@@ -472,6 +483,8 @@ struct RowPlan {
     int2* list;
     int32_t E, nblk, rows_per_block;
     int32_t blocks_per_window, groups_per_window;
+    int32_t* ep_counts;
+    int32_t ep_source, ep_sources, ep_cap, ep_L;
 };
 
 // Rows of the items. Workgroup g of window w takes kThreads items of the window. Every workgroup
@@ -528,7 +541,12 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
     if (tid == 0)
         eoff[E] = total;
     __syncthreads();
-    if (blockIdx.x == 0) {
+    const bool ep = rp.ep_counts != nullptr;
+    if (blockIdx.x == 0 && ep) {
+        for (int e = tid; e < E; e += kThreads)
+            rp.ep_counts[((int64_t)(e / rp.ep_L) * rp.ep_sources + rp.ep_source) * rp.ep_L +
+                         e % rp.ep_L] = (int32_t)(eoff[e + 1] - eoff[e]);
+    } else if (blockIdx.x == 0) {
         const int epr = E / co.N;
         for (int e = tid; e < E; e += kThreads) {
             co.expert_offsets[e] = (int32_t)eoff[e];
@@ -556,11 +574,19 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
     if ((uint32_t)e < (uint32_t)E) {
         const uint32_t pf =
             rp.prefix[(int64_t)e * rp.nblk + i / rp.rows_per_block] + rp.local_rank[i];
-        row = (int32_t)(eoff[e] + pf);
+        if (ep) {                                        // a row past the region is skipped
+            const int r = e / rp.ep_L;
+            const uint32_t pos = (eoff[e] - eoff[r * rp.ep_L]) + pf;
+            row = pos < (uint32_t)rp.ep_cap
+                      ? (int32_t)(((int64_t)r * rp.ep_sources + rp.ep_source) * rp.ep_cap + pos)
+                      : -1;
+        } else {
+            row = (int32_t)(eoff[e] + pf);
+        }
         rp.list[w0 + (qbase[e] + (int32_t)pf)] = make_int2(row, t);
     }
     rp.token_row[i] = row;
-    if ((uint32_t)row < (uint32_t)R)
+    if (!ep && (uint32_t)row < (uint32_t)R)
         rp.row_token[row] = t;
     if (i - w0 >= (int64_t)window_rows)                  // past the window's valid rows
         rp.list[i] = make_int2(-1, -1);
@@ -660,6 +686,84 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_layout_small(
     }
 }
 
+// ---------------------------------------------------------------------- expert-parallel receive --
+// Receiver half of dispatch for one rank, planning step. The S*L segments
+// (local expert l, source s) are taken in (l, s) order: segment (l, s) holds the
+// region_counts[(rank*S + s)*L + l] rows that source s wrote for expert rank*L + l, which start in
+// its region (rank, s) after its rows of lower experts. An exclusive scan of the segment sizes
+// gives the grouped layout (expert, source, token, slot); every grouped row g then finds its
+// segment by binary search and records its region row in grouped_src[g] (-1 past the last row).
+// Every workgroup repeats the (small) scan and takes its share of the grouped rows; workgroup 0
+// also writes the rank's per-expert counts and offsets. LDS: 3 * kMaxEpSegments u32.
+__global__ __launch_bounds__(kGroupThreads) void k_ep_recv_plan(
+    const int32_t* __restrict__ region_counts, int32_t rank, int32_t S, int32_t L, int32_t cap,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ grouped_src)
+{
+    constexpr int kPer = kMaxEpSegments / kGroupThreads;
+    __shared__ uint32_t cnt[kMaxEpSegments];             // source-major: s*L + l
+    __shared__ uint32_t srcoff[kMaxEpSegments];          // source-major: start in the region
+    __shared__ uint32_t dst[kMaxEpSegments + 1];         // (l, s) order: start in the grouped rows
+    __shared__ uint32_t wave_tot[kGroupWaves];
+    const int tid = threadIdx.x;
+    const int nseg = S * L;
+    for (int q = tid; q < nseg; q += kGroupThreads)
+        cnt[q] = (uint32_t)region_counts[(int64_t)rank * nseg + q];
+    __syncthreads();
+    for (int s = tid; s < S; s += kGroupThreads) {       // per-source scan over its experts
+        uint32_t run = 0u;
+        for (int l = 0; l < L; ++l) {
+            srcoff[s * L + l] = run;
+            run += cnt[s * L + l];
+        }
+    }
+    uint32_t v[kPer];
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int q = tid * kPer + u;                    // (l, s) order: q = l*S + s
+        v[u] = q < nseg ? cnt[(q % S) * L + q / S] : 0u;
+        mine += v[u];
+    }
+    uint32_t total = 0u;
+    uint32_t run = block_exclusive_scan<kGroupThreads>(mine, wave_tot, &total);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int q = tid * kPer + u;
+        if (q < nseg)
+            dst[q] = run;
+        run += v[u];
+    }
+    if (tid == 0)
+        dst[nseg] = total;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int l = tid; l < L; l += kGroupThreads) {
+            expert_offsets[l] = (int32_t)dst[l * S];
+            expert_counts[l] = (int32_t)(dst[(l + 1) * S] - dst[l * S]);
+        }
+        if (tid == 0)
+            expert_offsets[L] = (int32_t)total;
+    }
+    for (int64_t g = (int64_t)blockIdx.x * kGroupThreads + tid; g < (int64_t)S * cap;
+         g += (int64_t)gridDim.x * kGroupThreads) {
+        int32_t src = -1;
+        if (g < (int64_t)total) {
+            int lo = 0, hi = nseg - 1;                   // last q with dst[q] <= g
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (dst[mid] <= (uint32_t)g)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int s = lo % S, l = lo / S;
+            src = (int32_t)(((int64_t)rank * S + s) * cap + srcoff[s * L + l] + (g - dst[lo]));
+        }
+        grouped_src[g] = src;
+    }
+}
+
 // ----------------------------------------------------------------------------------- packing --
 // Wavefront placement of the row kernels. Wavefront w of workgroup blk handles item
 // m = (blk / 8) * waves_per_group + w of XCD blk % 8. Items of XCD x belong to tokens
@@ -691,8 +795,9 @@ enum PackOrder { PACK_TOKEN_ORDER = 0, PACK_WINDOWS = 1 };
 struct PackPlan {
     const int32_t* token_row;
     const int2* list;
-    int32_t T, k, R, pieces;
+    int32_t T, k, R, pieces;          // R = T*k items
     int32_t rows_per_window, nwin;
+    int64_t row_limit;                // rows of the destination buffer
 };
 
 // The (token, row, piece) of a wavefront: for TOKEN_ORDER the row is read by the caller after
@@ -728,7 +833,7 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
         if (xi.token < pp.nwin && pos < pp.R) {
             it.piece = xi.sub - q * pp.pieces;
             const int2 rt = pp.list[pos];
-            if ((uint32_t)rt.x < (uint32_t)pp.R) {
+            if ((uint64_t)(uint32_t)rt.x < (uint64_t)pp.row_limit && rt.x >= 0) {
                 it.row = rt.x;
                 it.token = rt.y;
             }
@@ -756,8 +861,44 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows(const u32x4* __re
     if (active)
         v = x[it.token * chunks_per_row + c];
     const int32_t row = ORDER == PACK_TOKEN_ORDER ? pp.token_row[it.index] : it.row;
-    if (active && (uint32_t)row < (uint32_t)pp.R)
+    if (active && row >= 0 && (int64_t)row < pp.row_limit)
         __builtin_nontemporal_store(v, recv + (int64_t)row * chunks_per_row + c);
+}
+
+// Copies of whole rows by a row map, grid-stride over (row, 1 KB piece) by wavefronts: GATHER
+// dst[g] = src[map[g]], SCATTER dst[map[g]] = src[g], for g < min(*n_rows, max_rows); a map
+// entry outside [0, row_limit) is skipped. The row count is read on the device (it is the output
+// of the previous kernel), so every wavefront's loop ends at the same bound.
+enum CopyDir { COPY_GATHER = 0, COPY_SCATTER = 1 };
+
+template <int DIR>
+__global__ __launch_bounds__(64 * kPackWaves) void k_copy_rows(const u32x4* __restrict__ src,
+                                                               u32x4* __restrict__ dst,
+                                                               int32_t chunks_per_row,
+                                                               int32_t pieces,
+                                                               const int32_t* __restrict__ map,
+                                                               const int32_t* __restrict__ n_rows,
+                                                               int64_t max_rows,
+                                                               int64_t row_limit)
+{
+    int64_t n = *n_rows;
+    n = n < 0 ? 0 : n > max_rows ? max_rows : n;
+    const int64_t waves = (int64_t)gridDim.x * kPackWaves;
+    const int lane = threadIdx.x & 63;
+    for (int64_t m = (int64_t)blockIdx.x * kPackWaves + (threadIdx.x >> 6); m < n * pieces;
+         m += waves) {
+        const int64_t g = m / pieces;
+        const int c = (int)(m - g * pieces) * 64 + lane;
+        const int32_t r = map[g];
+        if (r < 0 || (int64_t)r >= row_limit || c >= chunks_per_row)
+            continue;
+        if (DIR == COPY_GATHER)
+            __builtin_nontemporal_store(src[(int64_t)r * chunks_per_row + c],
+                                        dst + g * chunks_per_row + c);
+        else
+            __builtin_nontemporal_store(src[g * chunks_per_row + c],
+                                        dst + (int64_t)r * chunks_per_row + c);
+    }
 }
 
 // Eight consecutive elements of x as fp32.
@@ -833,7 +974,7 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
     packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
     for (int j = 0; j < pp.k; ++j) {
         const int32_t row = __builtin_amdgcn_readlane(my_row, j);
-        if ((uint32_t)row >= (uint32_t)pp.R)
+        if (row < 0 || (int64_t)row >= pp.row_limit)
             continue;                                    // uniform per wavefront
         if (active) {
             __builtin_nontemporal_store(packed,
@@ -1206,9 +1347,16 @@ CountOutputs count_outputs(const moe_dispatch_out_t* out, int32_t n_ranks)
 
 // Scan of the histograms, then the rows (whose workgroup 0 also writes the count outputs, so it
 // runs even for an empty batch).
+// Expert-parallel send: where the rows of one source go (its regions) and its region counts.
+struct EpSend {
+    int32_t* counts;
+    int32_t source, sources, cap, L;
+};
+
 void launch_scan_rows(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E,
-                      const moe_dispatch_out_t* out, int32_t n_ranks, const Workspace& ws,
-                      const LayoutPlan& plan, const WindowPlan& wp, hipStream_t stream)
+                      int32_t* token_row, int32_t* row_token, const CountOutputs& co,
+                      const EpSend* ep, const Workspace& ws, const LayoutPlan& plan,
+                      const WindowPlan& wp, hipStream_t stream)
 {
     const dim3 grid((unsigned)ceil_div(E, kGroupWaves));
     const int64_t s = ceil_div(plan.nblk, 64);
@@ -1231,23 +1379,28 @@ void launch_scan_rows(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E,
     rp.local_rank = ws.local_rank;
     rp.prefix = ws.prefix;
     rp.totals = ws.totals;
-    rp.token_row = out->token_row;
-    rp.row_token = out->row_token;
+    rp.token_row = token_row;
+    rp.row_token = row_token;
     rp.E = E;
     rp.nblk = plan.nblk;
     rp.rows_per_block = plan.rows_per_block;
     rp.list = ws.list;
     rp.blocks_per_window = wp.blocks_per_window;
     rp.groups_per_window = (int32_t)ceil_div(wp.rows_per_window, kThreads);
+    rp.ep_counts = ep ? ep->counts : nullptr;
+    rp.ep_source = ep ? ep->source : 0;
+    rp.ep_sources = ep ? ep->sources : 1;
+    rp.ep_cap = ep ? ep->cap : 0;
+    rp.ep_L = ep ? ep->L : 1;
     const int64_t want = (int64_t)wp.nwin * rp.groups_per_window;
-    k_layout_rows<<<(unsigned)(want < 1 ? 1 : want), kThreads, 0, stream>>>(
-        rp, R, k, count_outputs(out, n_ranks));
+    k_layout_rows<<<(unsigned)(want < 1 ? 1 : want), kThreads, 0, stream>>>(rp, R, k, co);
 }
 
 // Packing in token order (token_row given), or by windows from the list the rows kernel wrote.
 void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t k,
                  const int32_t* token_row, const int2* list, const WindowPlan* wp,
-                 moe_dtype_t payload_dtype, void* recv, float* recv_scales, hipStream_t stream)
+                 moe_dtype_t payload_dtype, void* recv, float* recv_scales, int64_t row_limit,
+                 hipStream_t stream)
 {
     const int32_t R = T * k;
     if (R == 0)
@@ -1263,6 +1416,7 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
     pp.pieces = (int32_t)ceil_div(fp8 ? H / 8 : cpr, 64);
     pp.rows_per_window = wp ? wp->rows_per_window : 0;
     pp.nwin = wp ? wp->nwin : 0;
+    pp.row_limit = row_limit;
     const bool windows = wp && (int64_t)pp.rows_per_window * pp.pieces < (int64_t)INT32_MAX / 2;
     const dim3 grid((unsigned)(windows ? xcd_blocks(pp.nwin, (int64_t)pp.rows_per_window *
                                                                  pp.pieces, kPackWaves)
@@ -1290,10 +1444,9 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
 
 template <typename YT, typename OT>
 void launch_combine_typed(const void* y, int32_t T, int32_t H, int32_t k,
-                          const int32_t* token_row, const float* topk_w, void* out,
+                          const int32_t* token_row, const float* topk_w, void* out, int32_t R,
                           hipStream_t stream)
 {
-    const int32_t R = T * k;
     const int32_t nseg = (int32_t)ceil_div(H / 8, 64);
     const dim3 grid((unsigned)ceil_div((int64_t)T * nseg, kCombineWaves));
     const YT* yp = static_cast<const YT*>(y);
@@ -1363,7 +1516,8 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, 
     const LayoutPlan plan = hist_plan(R);
     const Workspace ws = carve_workspace(workspace, T, E, k);
     launch_hist(topk_idx, R, E, ws, plan, stream);
-    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, window_plan(plan, 0, k),
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
+                     count_outputs(out, n_ranks), nullptr, ws, plan, window_plan(plan, 0, k),
                      stream);
     return launch_status();
 }
@@ -1379,7 +1533,7 @@ moe_status_t moe_dispatch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, in
     if (T == 0)
         return MOE_OK;
     launch_pack(x, x_dtype, T, H, k, token_row, nullptr, nullptr, payload_dtype, recv,
-                recv_scales, stream);
+                recv_scales, (int64_t)T * k, stream);
     return launch_status();
 }
 
@@ -1404,9 +1558,10 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
     const Workspace ws = carve_workspace(workspace, T, E, k);
     launch_hist(topk_idx, R, E, ws, plan, stream);
     const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
-    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, wp, stream);
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
+                     count_outputs(out, n_ranks), nullptr, ws, plan, wp, stream);
     launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
-                out->recv_scales, stream);
+                out->recv_scales, R, stream);
     return launch_status();
 }
 
@@ -1437,7 +1592,7 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
                          topk_idx, topk_w, out->token_row, out->row_token,
                          count_outputs(out, n_ranks));
         launch_pack(x, x_dtype, T, H, k, out->token_row, nullptr, nullptr, payload_dtype,
-                    out->recv, out->recv_scales, stream);
+                    out->recv, out->recv_scales, R, stream);
         return launch_status();
     }
     const Workspace ws = carve_workspace(workspace, T, E, k);
@@ -1452,17 +1607,19 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
         launch_hist(topk_idx, R, E, ws, plan, stream);
     }
     const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
-    launch_scan_rows(topk_idx, (int32_t)R, k, E, out, n_ranks, ws, plan, wp, stream);
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
+                     count_outputs(out, n_ranks), nullptr, ws, plan, wp, stream);
     launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
-                out->recv_scales, stream);
+                out->recv_scales, R, stream);
     return launch_status();
 }
 
-moe_status_t moe_combine(const void* y, moe_dtype_t y_dtype, int32_t T, int32_t H, int32_t k,
-                         const int32_t* token_row, const float* topk_w, void* out,
-                         moe_dtype_t out_dtype, hipStream_t stream)
+static moe_status_t combine_checked(const void* y, moe_dtype_t y_dtype, int32_t T, int32_t H,
+                                    int32_t k, const int32_t* token_row, const float* topk_w,
+                                    void* out, moe_dtype_t out_dtype, int32_t y_rows,
+                                    hipStream_t stream)
 {
-    if (T < 0 || H < 1 || k < 1 || (int64_t)T * k > INT32_MAX)
+    if (T < 0 || H < 1 || k < 1 || (int64_t)T * k > INT32_MAX || y_rows < 0)
         return MOE_ERR_INVALID;
     if (!is_wide(y_dtype) || !is_wide(out_dtype))
         return MOE_ERR_UNSUPPORTED;
@@ -1475,14 +1632,173 @@ moe_status_t moe_combine(const void* y, moe_dtype_t y_dtype, int32_t T, int32_t 
     if (T == 0)
         return MOE_OK;
     if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16)
-        launch_combine_typed<uint16_t, uint16_t>(y, T, H, k, token_row, topk_w, out, stream);
+        launch_combine_typed<uint16_t, uint16_t>(y, T, H, k, token_row, topk_w, out, y_rows,
+                                                 stream);
     else if (y_dtype == MOE_BF16)
-        launch_combine_typed<uint16_t, float>(y, T, H, k, token_row, topk_w, out, stream);
+        launch_combine_typed<uint16_t, float>(y, T, H, k, token_row, topk_w, out, y_rows, stream);
     else if (out_dtype == MOE_BF16)
-        launch_combine_typed<float, uint16_t>(y, T, H, k, token_row, topk_w, out, stream);
+        launch_combine_typed<float, uint16_t>(y, T, H, k, token_row, topk_w, out, y_rows, stream);
     else
-        launch_combine_typed<float, float>(y, T, H, k, token_row, topk_w, out, stream);
+        launch_combine_typed<float, float>(y, T, H, k, token_row, topk_w, out, y_rows, stream);
     return launch_status();
+}
+
+moe_status_t moe_combine(const void* y, moe_dtype_t y_dtype, int32_t T, int32_t H, int32_t k,
+                         const int32_t* token_row, const float* topk_w, void* out,
+                         moe_dtype_t out_dtype, hipStream_t stream)
+{
+    if ((int64_t)T * k > INT32_MAX)
+        return MOE_ERR_INVALID;
+    return combine_checked(y, y_dtype, T, H, k, token_row, topk_w, out, out_dtype, T * k, stream);
+}
+
+// ------------------------------------------------------------------- expert parallelism (one GPU)
+int64_t moe_ep_capacity(int32_t T, int32_t E, int32_t k, int32_t n_ranks)
+{
+    if (T < 0 || E < 1 || k < 1 || n_ranks < 1 || E % n_ranks != 0)
+        return 0;
+    const int32_t L = E / n_ranks;
+    return (int64_t)T * (k < L ? k : L);
+}
+
+static moe_status_t ep_region_args(int32_t E, int32_t n_ranks, int32_t n_sources, int32_t cap)
+{
+    if (E < 1 || n_ranks < 1 || E % n_ranks != 0 || n_sources < 1 || cap < 0)
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)n_ranks * n_sources * cap > INT32_MAX)
+        return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+moe_status_t moe_ep_send(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H,
+                         const int32_t* topk_idx, int32_t k, int32_t E, int32_t n_ranks,
+                         int32_t source, int32_t n_sources, int32_t cap, void* regions,
+                         int32_t* region_counts, int32_t* send_row, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream)
+{
+    moe_status_t st = ep_region_args(E, n_ranks, n_sources, cap);
+    if (st != MOE_OK)
+        return st;
+    if (T < 0 || k < 1 || (int64_t)T * k > INT32_MAX || source < 0 || source >= n_sources)
+        return MOE_ERR_INVALID;
+    if ((int64_t)cap < moe_ep_capacity(T, E, k, n_ranks))
+        return MOE_ERR_INVALID;
+    if (!region_counts || (T > 0 && (!topk_idx || !send_row)))
+        return MOE_ERR_INVALID;
+    st = check_pack_args(x, x_dtype, T, H, k, send_row, x_dtype, regions, nullptr);
+    if (st != MOE_OK)
+        return st;
+    if (!workspace || workspace_bytes < moe_dispatch_workspace_bytes(T, E, k))
+        return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t R = (int64_t)T * k;
+    const LayoutPlan plan = hist_plan(R);
+    const Workspace ws = carve_workspace(workspace, T, E, k);
+    EpSend ep;
+    ep.counts = region_counts;
+    ep.source = source;
+    ep.sources = n_sources;
+    ep.cap = cap;
+    ep.L = E / n_ranks;
+    launch_hist(topk_idx, R, E, ws, plan, stream);
+    const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
+    const CountOutputs none = {};
+    launch_scan_rows(topk_idx, (int32_t)R, k, E, send_row, nullptr, none, &ep, ws, plan, wp,
+                     stream);
+    launch_pack(x, x_dtype, T, H, k, send_row, ws.list, &wp, x_dtype, regions, nullptr,
+                (int64_t)n_ranks * n_sources * cap, stream);
+    return launch_status();
+}
+
+static moe_status_t ep_rank_args(moe_dtype_t dtype, int32_t H, int32_t E, int32_t n_ranks,
+                                 int32_t n_sources, int32_t cap, const void* a, const void* b)
+{
+    moe_status_t st = ep_region_args(E, n_ranks, n_sources, cap);
+    if (st != MOE_OK)
+        return st;
+    if (H < 1)
+        return MOE_ERR_INVALID;
+    if (!is_wide(dtype) || ((int64_t)H * (int64_t)dtype_size(dtype)) % 16 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)n_sources * (E / n_ranks) > kMaxEpSegments)
+        return MOE_ERR_UNSUPPORTED;
+    if (!aligned(a, 16) || !aligned(b, 16))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+static void launch_copy_rows(int DIR, const void* src, void* dst, moe_dtype_t dtype, int32_t H,
+                             const int32_t* map, const int32_t* n_rows, int64_t max_rows,
+                             int64_t row_limit, hipStream_t stream)
+{
+    const int32_t cpr = (int32_t)((int64_t)H * (int64_t)dtype_size(dtype) / 16);
+    const int32_t pieces = (int32_t)ceil_div(cpr, 64);
+    // grid-stride: 2048 workgroups (32768 wavefronts) cover the GPU; the row count is only known
+    // on the device, so a grid sized for max_rows would mostly start idle wavefronts
+    int64_t blocks = ceil_div(max_rows * pieces, kPackWaves);
+    blocks = blocks < 1 ? 1 : blocks > 2048 ? 2048 : blocks;
+    const u32x4* s = static_cast<const u32x4*>(src);
+    u32x4* d = static_cast<u32x4*>(dst);
+    if (DIR == COPY_GATHER)
+        k_copy_rows<COPY_GATHER><<<(unsigned)blocks, 64 * kPackWaves, 0, stream>>>(
+            s, d, cpr, pieces, map, n_rows, max_rows, row_limit);
+    else
+        k_copy_rows<COPY_SCATTER><<<(unsigned)blocks, 64 * kPackWaves, 0, stream>>>(
+            s, d, cpr, pieces, map, n_rows, max_rows, row_limit);
+}
+
+moe_status_t moe_ep_recv(const void* regions, moe_dtype_t dtype, int32_t H, int32_t E,
+                         int32_t n_ranks, int32_t rank, int32_t n_sources, int32_t cap,
+                         const int32_t* region_counts, void* grouped, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* grouped_src, hipStream_t stream)
+{
+    moe_status_t st = ep_rank_args(dtype, H, E, n_ranks, n_sources, cap, regions, grouped);
+    if (st != MOE_OK)
+        return st;
+    if (rank < 0 || rank >= n_ranks)
+        return MOE_ERR_INVALID;
+    if (!region_counts || !expert_counts || !expert_offsets ||
+        (cap > 0 && (!regions || !grouped || !grouped_src)))
+        return MOE_ERR_INVALID;
+    const int32_t L = E / n_ranks;
+    int64_t plan_blocks = ceil_div((int64_t)n_sources * cap, 4 * kGroupThreads);
+    plan_blocks = plan_blocks < 1 ? 1 : plan_blocks > 64 ? 64 : plan_blocks;
+    k_ep_recv_plan<<<(unsigned)plan_blocks, kGroupThreads, 0, stream>>>(
+        region_counts, rank, n_sources, L, cap, expert_counts, expert_offsets, grouped_src);
+    if (cap > 0)
+        launch_copy_rows(COPY_GATHER, regions, grouped, dtype, H, grouped_src, expert_offsets + L,
+                         (int64_t)n_sources * cap, (int64_t)n_ranks * n_sources * cap, stream);
+    return launch_status();
+}
+
+moe_status_t moe_ep_return(const void* y_grouped, moe_dtype_t dtype, int32_t H, int32_t E,
+                           int32_t n_ranks, int32_t n_sources, int32_t cap,
+                           const int32_t* grouped_src, const int32_t* expert_offsets,
+                           void* returns, hipStream_t stream)
+{
+    moe_status_t st = ep_rank_args(dtype, H, E, n_ranks, n_sources, cap, y_grouped, returns);
+    if (st != MOE_OK)
+        return st;
+    if (cap == 0)
+        return MOE_OK;
+    if (!y_grouped || !grouped_src || !expert_offsets || !returns)
+        return MOE_ERR_INVALID;
+    launch_copy_rows(COPY_SCATTER, y_grouped, returns, dtype, H, grouped_src,
+                     expert_offsets + E / n_ranks, (int64_t)n_sources * cap,
+                     (int64_t)n_ranks * n_sources * cap, stream);
+    return launch_status();
+}
+
+moe_status_t moe_ep_combine(const void* returns, moe_dtype_t y_dtype, int32_t T, int32_t H,
+                            int32_t k, const int32_t* send_row, const float* topk_w,
+                            int32_t region_rows, void* out, moe_dtype_t out_dtype,
+                            hipStream_t stream)
+{
+    return combine_checked(returns, y_dtype, T, H, k, send_row, topk_w, out, out_dtype,
+                           region_rows, stream);
 }
 
 }  // extern "C"

@@ -166,6 +166,74 @@ moe_status_t moe_combine(const void* y, moe_dtype_t y_dtype, int32_t T, int32_t 
                          const int32_t* token_row, const float* topk_w, void* out,
                          moe_dtype_t out_dtype, hipStream_t stream);
 
+/*
+ * Expert parallelism over several devices, emulated on one GPU. The pages split dispatch and
+ * combine into a sender half and a receiver half ("MoE all-to-all over EFA"), size each receive
+ * buffer for the worst case before any row is written and let every sender write its rows
+ * straight into the receiver's buffer ("Verzend- en ontvangstbuffers"); the receiver then copies
+ * the rows into the input of its grouped GEMM, and combine returns the expert outputs to their
+ * senders ("Dispatch en Combine"). Here S sources (the devices that own tokens) send to N ranks
+ * (rank r hosts the L = E/N experts [r*L, (r+1)*L)), all in device memory of one GPU:
+ *   - the region array [N*S*cap, H] holds one region of `cap` rows per (rank r, source s), at rows
+ *     [(r*S + s)*cap, (r*S + s + 1)*cap); `cap` >= moe_ep_capacity(T, E, k, N);
+ *   - region_counts [N, S, L] int32: rows source s wrote for expert r*L + l, at (r*S + s)*L + l.
+ * One step: moe_ep_send for every source, moe_ep_recv for every rank, the experts, moe_ep_return
+ * for every rank, moe_ep_combine for every source. Calls for different sources (or ranks) write
+ * disjoint memory.
+ */
+
+/* Rows of one (rank, source) region: T * min(k, E/N), the most one source can send to one rank
+ * (each token at most once per hosted expert). Returns 0 for invalid sizes. */
+int64_t moe_ep_capacity(int32_t T, int32_t E, int32_t k, int32_t n_ranks);
+
+/*
+ * moe_ep_send -- sender half of dispatch for source `source` (0 <= source < n_sources).
+ *   x [T, H] (MOE_F32 or MOE_BF16, 16-byte aligned rows), topk_idx [T, k] ids in [0, E).
+ *   Writes into `regions` (x's format; only this source's regions) the rows of every (token, slot):
+ *   region (r, source) holds its rows to rank r ordered by (expert, token, slot); writes
+ *   region_counts[(r*S + source)*L + l] for every r, l, and send_row[t*k + j] = the region-array row
+ *   of (t, j). Uses a workspace of moe_dispatch_workspace_bytes(T, E, k) bytes.
+ * Requires cap >= moe_ep_capacity(T, E, k, n_ranks) and N*S*cap < 2^31 (else MOE_ERR_INVALID).
+ */
+moe_status_t moe_ep_send(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H,
+                         const int32_t* topk_idx, int32_t k, int32_t E, int32_t n_ranks,
+                         int32_t source, int32_t n_sources, int32_t cap, void* regions,
+                         int32_t* region_counts, int32_t* send_row, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_ep_recv -- receiver half of dispatch for rank `rank`: copies the rows of its S regions into
+ * `grouped` [S*cap, H] ordered by (local expert, source, token, slot), writes expert_counts [L],
+ * expert_offsets [L+1] (offsets in `grouped`; [L] = rows received) and grouped_src [S*cap]: the
+ * region-array row of each grouped row (-1 past the last one). Reads region_counts (all sources'
+ * sends to this rank must be complete, i.e. enqueued earlier on the same stream).
+ * Requires S*L <= 4096 (else MOE_ERR_UNSUPPORTED).
+ */
+moe_status_t moe_ep_recv(const void* regions, moe_dtype_t dtype, int32_t H, int32_t E,
+                         int32_t n_ranks, int32_t rank, int32_t n_sources, int32_t cap,
+                         const int32_t* region_counts, void* grouped, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* grouped_src, hipStream_t stream);
+
+/*
+ * moe_ep_return -- receiver half of combine: every grouped row of expert output y_grouped
+ * [S*cap, H] goes back to its region row, returns[grouped_src[g]] = y_grouped[g], for
+ * g < expert_offsets[L] (both from moe_ep_recv). `returns` has the region array's layout.
+ */
+moe_status_t moe_ep_return(const void* y_grouped, moe_dtype_t dtype, int32_t H, int32_t E,
+                           int32_t n_ranks, int32_t n_sources, int32_t cap,
+                           const int32_t* grouped_src, const int32_t* expert_offsets,
+                           void* returns, hipStream_t stream);
+
+/*
+ * moe_ep_combine -- sender half of combine for one source: moe_combine over the returned rows,
+ * out[t, h] = sum_j w[t, j] * returns[send_row[t*k + j], h] (fp32 accumulation in slot order).
+ *   region_rows = N*S*cap, the rows of `returns`; a send_row outside [0, region_rows) is skipped.
+ */
+moe_status_t moe_ep_combine(const void* returns, moe_dtype_t y_dtype, int32_t T, int32_t H,
+                            int32_t k, const int32_t* send_row, const float* topk_w,
+                            int32_t region_rows, void* out, moe_dtype_t out_dtype,
+                            hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_str(moe_status_t status);
 

@@ -407,7 +407,8 @@ int oracle_combine(const void* y, int32_t y_dtype, int32_t T, int32_t H, int32_t
  * Combine"). Readings:
  *   - the receive buffer of rank r holds one region of `cap` rows per source s, at rows
  *     [(r*S + s)*cap, (r*S + s + 1)*cap) of one [N*S*cap, H] array; cap >= T*min(k, L), the most
- *     rows one source can send to one rank (each token at most once per hosted expert);
+ *     rows one source can send to one rank when a token's experts are distinct (ids repeated
+ *     within a token that overflow a region are rejected);
  *   - inside its region a source's rows are ordered by (local expert, token, slot), and the
  *     source publishes region_counts[(r*S + s)*L + l], its rows for expert r*L + l;
  *   - the receiver's grouped layout is ordered by (local expert, source, token, slot);
@@ -438,6 +439,13 @@ int oracle_ep_send(const void* x, int32_t x_dtype, int32_t T, int32_t H, const i
     for (int64_t i = 0; i < R; i++) {
         const int e = topk_idx[i];
         region_counts[((int64_t)(e / L) * S + source) * L + e % L]++;
+    }
+    for (int r = 0; r < N; r++) {                      /* ids repeated in a token can overflow */
+        int64_t n = 0;
+        for (int l = 0; l < L; l++)
+            n += region_counts[((int64_t)r * S + source) * L + l];
+        if (n > cap)
+            return 1;
     }
     orc_item_t* items = (orc_item_t*)malloc((size_t)(R > 0 ? R : 1) * sizeof(orc_item_t));
     if (!items)

@@ -28,7 +28,9 @@ def test_library_loads_and_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["moe_combine", "moe_dispatch", "moe_dispatch_layout",
                             "moe_dispatch_pack", "moe_dispatch_workspace_bytes",
-                            "moe_route_dispatch", "moe_route_topk", "moe_status_str"])
+                            "moe_route_dispatch", "moe_route_topk", "moe_status_str",
+                            "moe_ep_capacity", "moe_ep_send", "moe_ep_recv", "moe_ep_return",
+                            "moe_ep_combine"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -171,6 +173,49 @@ def test_route_dispatch_validation_checks_every_part():
     assert call(wsb=need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(ws=None) == moe.MOE_ERR_WORKSPACE
     assert call(ws=MIS) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_ep_capacity_and_validation():
+    lib = moe.load()
+    assert lib.moe_ep_capacity(512, 384, 8, 8) == 512 * 8
+    assert lib.moe_ep_capacity(10, 8, 2, 8) == 10 * 1              # one expert per rank
+    assert lib.moe_ep_capacity(10, 8, 2, 3) == 0                   # E % N
+    F32, BF16, FP8 = moe.MOE_F32, moe.MOE_BF16, moe.MOE_FP8_E4M3
+    need = moe.moe_dispatch_workspace_bytes(10, 8, 2)
+    send = lib.moe_ep_send
+    ok = dict(x=A16, xd=F32, T=10, H=256, idx=A16, k=2, E=8, N=4, src=1, S=3, cap=20, reg=A16b,
+              cnt=A16, row=A16, ws=A16, wsb=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return send(a["x"], a["xd"], a["T"], a["H"], a["idx"], a["k"], a["E"], a["N"], a["src"],
+                    a["S"], a["cap"], a["reg"], a["cnt"], a["row"], a["ws"], a["wsb"], S0)
+
+    assert call(cap=19) == moe.MOE_ERR_INVALID                       # below the worst case
+    assert call(src=3) == moe.MOE_ERR_INVALID                        # source >= S
+    assert call(src=-1) == moe.MOE_ERR_INVALID
+    assert call(N=3) == moe.MOE_ERR_INVALID                          # E % N
+    assert call(cnt=None) == moe.MOE_ERR_INVALID
+    assert call(row=None) == moe.MOE_ERR_INVALID
+    assert call(xd=FP8) == moe.MOE_ERR_UNSUPPORTED
+    assert call(reg=MIS) == moe.MOE_ERR_UNSUPPORTED
+    assert call(wsb=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(S=2 ** 16, cap=2 ** 16) == moe.MOE_ERR_INVALID       # N*S*cap >= 2^31
+    recv = lib.moe_ep_recv
+    assert recv(A16, BF16, 256, 8, 4, 4, 3, 20, A16, A16b, A16, A16, A16, S0) == \
+        moe.MOE_ERR_INVALID                                          # rank >= N
+    assert recv(A16, FP8, 256, 8, 4, 0, 3, 20, A16, A16b, A16, A16, A16, S0) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert recv(A16, BF16, 256, 1024, 1, 0, 8, 20, A16, A16b, A16, A16, A16, S0) == \
+        moe.MOE_ERR_UNSUPPORTED                                      # S*L > 4096
+    assert recv(A16, BF16, 256, 8, 4, 0, 3, 20, None, A16b, A16, A16, A16, S0) == \
+        moe.MOE_ERR_INVALID
+    ret = lib.moe_ep_return
+    assert ret(A16, BF16, 256, 8, 4, 3, 20, None, A16, A16b, S0) == moe.MOE_ERR_INVALID
+    assert ret(MIS, BF16, 256, 8, 4, 3, 20, A16, A16, A16b, S0) == moe.MOE_ERR_UNSUPPORTED
+    comb = lib.moe_ep_combine
+    assert comb(A16, BF16, 4, 256, 2, A16, A16, -1, A16b, BF16, S0) == moe.MOE_ERR_INVALID
+    assert comb(None, BF16, 0, 256, 2, None, None, 0, None, BF16, S0) == moe.MOE_OK
 
 
 def test_combine_validation():

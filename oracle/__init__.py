@@ -56,6 +56,9 @@ def _load():
             "oracle_ep_send": [P, I, I, I, P, I, I, I, I, I, I, P, P, P],
             "oracle_ep_recv": [P, I, I, I, I, I, I, I, P, P, P, P, P],
             "oracle_ep_return": [P, I, I, L, P, P],
+            "oracle_ep_partial_rows": [P, I, I, I, I, I, I, I, P, P],
+            "oracle_ep_reduce": [P, I, I, I, I, I, I, I, P, I, I, P, P, P, P, P],
+            "oracle_ep_combine_reduced": [P, I, I, I, I, P, P, I],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -227,3 +230,52 @@ def ep_return(y_grouped, dtype: str, grouped_src, returns) -> None:
                                   _p(_c(grouped_src, np.int32)), _p(returns))
     if rc:
         raise ValueError(f"oracle_ep_return rejected its arguments (code {rc})")
+
+
+# Combine with pre-reduction on the expert side: rank r sends one partial row per (token, rank),
+# the source adds the partial rows of each token.
+
+def ep_partial_rows(topk_idx, E: int, N: int, source: int, S: int, pcap: int, part_counts):
+    """part_row int32 [T, N] (partial-array row of (token, rank), -1 if the token has no expert
+    on the rank); fills part_counts [N, S] column `source` in place."""
+    topk_idx = _c(topk_idx, np.int32)
+    T, k = topk_idx.shape
+    part_row = np.empty((T, N), np.int32)
+    assert part_counts.flags.c_contiguous and part_counts.dtype == np.int32
+    rc = _load().oracle_ep_partial_rows(_p(topk_idx), T, k, E, N, source, S, pcap, _p(part_row),
+                                        _p(part_counts))
+    if rc:
+        raise ValueError(f"oracle_ep_partial_rows rejected its arguments (code {rc})")
+    return part_row
+
+
+def ep_reduce(y_grouped, dtype: str, E: int, N: int, rank: int, S: int, cap: int, grouped_src,
+              topk_idx, topk_w, send_row, part_row, partials) -> None:
+    """Partial rows of one rank for all sources, written into `partials` in place. The source
+    tables are stacked: source s owns tokens [s*T, (s+1)*T)."""
+    y_grouped = _c(y_grouped, NP_DTYPES[dtype])
+    topk_idx = _c(topk_idx, np.int32)
+    TT, k = topk_idx.shape
+    T = TT // S
+    H = y_grouped.shape[1]
+    assert partials.flags.c_contiguous and partials.dtype == NP_DTYPES[dtype]
+    rc = _load().oracle_ep_reduce(
+        _p(y_grouped), DTYPES[dtype], H, E, N, rank, S, cap, _p(_c(grouped_src, np.int32)), T, k,
+        _p(topk_idx), _p(_c(topk_w, np.float32)), _p(_c(send_row, np.int32)),
+        _p(_c(part_row, np.int32)), _p(partials))
+    if rc:
+        raise ValueError(f"oracle_ep_reduce rejected its arguments (code {rc})")
+
+
+def ep_combine_reduced(partials, dtype: str, part_row, out_dtype: str) -> np.ndarray:
+    """out[t] = sum over ranks of the token's partial rows, rounded once."""
+    partials = _c(partials, NP_DTYPES[dtype])
+    part_row = _c(part_row, np.int32)
+    T, N = part_row.shape
+    H = partials.shape[1]
+    out = np.empty((T, H), NP_DTYPES[out_dtype])
+    rc = _load().oracle_ep_combine_reduced(_p(partials), DTYPES[dtype], T, H, N, _p(part_row),
+                                           _p(out), DTYPES[out_dtype])
+    if rc:
+        raise ValueError(f"oracle_ep_combine_reduced rejected its arguments (code {rc})")
+    return out

@@ -525,3 +525,114 @@ int oracle_ep_return(const void* y_grouped, int32_t dtype, int32_t H, int64_t n_
                    rb);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Combine with pre-reduction on the expert side ("Evaluatie / Dispatch/Combine-latentie": the pages
+ * accumulate only on the receiver, which is why they lag at prefill). Reading: before the return
+ * trip, rank r sums, for every token t of source s that has experts on r, the weighted outputs of
+ * those experts into one partial row, P[r, s, t] = sum over slots j with rank(idx[t, j]) = r of
+ * w[t, j] * y(t, j), rounded once to the wire format; only partial rows travel back, and the
+ * source finishes out[t] = sum over ranks of P[r, s, t], rounded once.
+ *   - the partial rows of (rank r, source s) sit in a region of pcap >= T rows at rows
+ *     [(r*S + s)*pcap, ...) of the partial array, one row per token of s with experts on r, in
+ *     token order; part_row[t*N + r] is that row, or -1 when t has no expert on r;
+ *   - sums are exact (double) and rounded once, at the partial and at the output.
+ * ---------------------------------------------------------------------------------------------- */
+
+/* Where the partial rows of source `source` go: part_row [T, N] and part_counts[r*S + source]. */
+int oracle_ep_partial_rows(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t N,
+                           int32_t source, int32_t S, int32_t pcap, int32_t* part_row,
+                           int32_t* part_counts)
+{
+    if (T < 0 || k < 1 || E < 1 || N < 1 || E % N != 0 || S < 1 || source < 0 || source >= S ||
+        pcap < T)
+        return 1;
+    const int32_t L = E / N;
+    for (int r = 0; r < N; r++) {
+        int32_t p = 0;
+        for (int64_t t = 0; t < T; t++) {
+            int on_rank = 0;
+            for (int j = 0; j < k; j++)
+                if (topk_idx[t * k + j] / L == r)
+                    on_rank = 1;
+            part_row[t * N + r] = on_rank ? (int32_t)(((int64_t)r * S + source) * pcap + p) : -1;
+            p += on_rank;
+        }
+        part_counts[(int64_t)r * S + source] = p;
+    }
+    return 0;
+}
+
+/* Expert side: the partial rows of rank `rank` for every source. y_grouped holds the rank's
+ * expert outputs in its grouped layout and grouped_src (from receive) names each grouped row's
+ * region row; topk_idx / topk_w / send_row / part_row are the sources' tables, source s at
+ * [s*T, (s+1)*T) tokens. */
+int oracle_ep_reduce(const void* y_grouped, int32_t dtype, int32_t H, int32_t E, int32_t N,
+                     int32_t rank, int32_t S, int32_t cap, const int32_t* grouped_src, int32_t T,
+                     int32_t k, const int32_t* topk_idx, const float* topk_w,
+                     const int32_t* send_row, const int32_t* part_row, void* partials)
+{
+    if (H < 1 || E < 1 || N < 1 || E % N != 0 || S < 1 || rank < 0 || rank >= N || T < 0 ||
+        k < 1 || dtype == ORC_FP8_E4M3)
+        return 1;
+    const int32_t L = E / N;
+    /* grouped row of every region row of this rank */
+    const int64_t base = (int64_t)rank * S * cap, nreg = (int64_t)S * cap;
+    int64_t* grouped_of = (int64_t*)malloc((size_t)(nreg > 0 ? nreg : 1) * sizeof(int64_t));
+    if (!grouped_of)
+        return 2;
+    for (int64_t q = 0; q < nreg; q++)
+        grouped_of[q] = -1;
+    for (int64_t g = 0; g < nreg; g++)
+        if (grouped_src[g] >= 0)
+            grouped_of[grouped_src[g] - base] = g;
+    for (int s = 0; s < S; s++)
+        for (int64_t t = 0; t < T; t++) {
+            const int64_t tt = (int64_t)s * T + t;
+            const int32_t pr = part_row[tt * N + rank];
+            if (pr < 0)
+                continue;
+            for (int64_t h = 0; h < H; h++) {
+                double acc = 0.0;
+                for (int j = 0; j < k; j++) {
+                    if (topk_idx[tt * k + j] / L != rank)
+                        continue;
+                    const int64_t q = send_row[tt * k + j] - base;
+                    const int64_t g = (q >= 0 && q < nreg) ? grouped_of[q] : -1;
+                    if (g < 0) {
+                        free(grouped_of);
+                        return 1;
+                    }
+                    acc += (double)topk_w[tt * k + j] * load_elem(y_grouped, dtype, g * H + h);
+                }
+                if (dtype == ORC_F32)
+                    ((float*)partials)[(int64_t)pr * H + h] = (float)acc;
+                else
+                    ((uint16_t*)partials)[(int64_t)pr * H + h] = bf16_bits_from_double(acc);
+            }
+        }
+    free(grouped_of);
+    return 0;
+}
+
+/* Source side: out[t] = sum over ranks of the partial rows of token t, rounded once. */
+int oracle_ep_combine_reduced(const void* partials, int32_t dtype, int32_t T, int32_t H, int32_t N,
+                              const int32_t* part_row, void* out, int32_t out_dtype)
+{
+    if (T < 0 || H < 1 || N < 1 || dtype == ORC_FP8_E4M3 || out_dtype == ORC_FP8_E4M3)
+        return 1;
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t h = 0; h < H; h++) {
+            double acc = 0.0;
+            for (int r = 0; r < N; r++) {
+                const int32_t pr = part_row[t * N + r];
+                if (pr >= 0)
+                    acc += load_elem(partials, dtype, (int64_t)pr * H + h);
+            }
+            if (out_dtype == ORC_F32)
+                ((float*)out)[t * H + h] = (float)acc;
+            else
+                ((uint16_t*)out)[t * H + h] = bf16_bits_from_double(acc);
+        }
+    return 0;
+}

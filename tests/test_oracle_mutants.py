@@ -51,8 +51,16 @@ MUTANTS = {
     "ep_recv_region_start": ("for (int q = 0; q < l; q++)\n                start += c[q];",
                              "for (int q = 0; q + 1 < l; q++)\n                start += c[q];",
                              "test_oracle_ep.py"),
-    "ep_return_skips_row_zero": ("if (grouped_src[g] >= 0)", "if (grouped_src[g] > 0)",
+    "ep_return_skips_row_zero": ("if (grouped_src[g] >= 0)\n            memcpy(",
+                                 "if (grouped_src[g] > 0)\n            memcpy(",
                                  "test_oracle_ep.py"),
+    "ep_reduce_sums_every_slot": ("if (topk_idx[tt * k + j] / L != rank)\n",
+                                  "if (topk_idx[tt * k + j] / L != rank && 0)\n",
+                                  "test_oracle_ep_reduce.py"),
+    "ep_partial_rows_source_major": (
+        "part_row[t * N + r] = on_rank ? (int32_t)(((int64_t)r * S + source) * pcap + p) : -1;",
+        "part_row[t * N + r] = on_rank ? (int32_t)(((int64_t)source * N + r) * pcap + p) : -1;",
+        "test_oracle_ep_reduce.py"),
 }
 
 

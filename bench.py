@@ -348,6 +348,55 @@ def ep_emulation(torch, moe, dev, K):
         torch.cuda.synchronize()
         for p, ph in enumerate(order):
             tot[ph] += e[p].elapsed_time(e[p + 1])
+    # combine with pre-reduction on the expert side: partial-row layout (per source), the partial
+    # rows (per rank), the source-side finish; against the return + combine above
+    pcap = T
+    pc = torch.zeros((N, S), dtype=torch.int32, device=dev)
+    prow = [torch.empty((T, N), dtype=torch.int32, device=dev) for _ in range(S)]
+    prow_all = torch.empty((S * T, N), dtype=torch.int32, device=dev)
+    rows_all = torch.empty(S * T * k, dtype=torch.int32, device=dev)
+    partials = torch.zeros((N * S * pcap, H), dtype=torch.bfloat16, device=dev)
+    rws = moe.moe_ep_reduce_workspace(S, cap, dev)
+    out_red = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(S)]
+    red = {"partial_rows": [], "reduce": [], "finish": []}
+    for s in range(S):
+        red["partial_rows"].append(Prepared(
+            lib.moe_ep_partial_rows, P(idx[s * T:].data_ptr()), T, k, w.E, N, s, S, pcap,
+            P(prow[s].data_ptr()), P(pc.data_ptr()), stream))
+        red["finish"].append(Prepared(
+            lib.moe_ep_combine_reduced, P(partials.data_ptr()), B, T, H, N, P(prow[s].data_ptr()),
+            N * S * pcap, P(out_red[s].data_ptr()), B, stream))
+    for r in range(N):
+        red["reduce"].append(Prepared(
+            lib.moe_ep_reduce, P(grouped[r].data_ptr()), B, H, w.E, N, r, S, cap,
+            P(gs[r].data_ptr()), T, k, P(idx.data_ptr()), P(wt.data_ptr()),
+            P(rows_all.data_ptr()), P(prow_all.data_ptr()), pcap, P(partials.data_ptr()),
+            P(rws.data_ptr()), rws.numel(), stream))
+    for c in red["partial_rows"]:
+        c()
+    torch.cuda.synchronize()
+    torch.cat(prow, out=prow_all)
+    torch.cat(rows, out=rows_all)
+    rorder = ("partial_rows", "reduce", "finish")
+    for ph in rorder:
+        for c in red[ph]:
+            c()
+    torch.cuda.synchronize()
+    rtot = {ph: 0.0 for ph in rorder}
+    for _ in range(K):
+        e[0].record()
+        for p, ph in enumerate(rorder):
+            for c in red[ph]:
+                c()
+            e[p + 1].record()
+        torch.cuda.synchronize()
+        for p, ph in enumerate(rorder):
+            rtot[ph] += e[p].elapsed_time(e[p + 1])
+    full_o = torch.cat(out).view(torch.int16).to(torch.int32)
+    red_o = torch.cat(out_red).view(torch.int16).to(torch.int32)
+    mono = lambda v: torch.where(v < 0, -(v & 0x7FFF), v)  # noqa: E731
+    dist = (mono(full_o) - mono(red_o)).abs()
+    rows_back = int(pc.sum().item())
     b = 2
     rows_total = S * T * k
     alg = {"send": S * (T * H * b + T * k * H * b + 8 * T * k),
@@ -362,7 +411,15 @@ def ep_emulation(torch, moe, dev, K):
             "per_call_us": per_call,
             "phase_GBps": {ph: round(alg[ph] / (tot[ph] / K * 1e-3) / 1e9, 1) for ph in order},
             "algorithmic_bytes": alg,
-            "GBps": round(sum(alg.values()) / (step_ms * 1e-3) / 1e9, 1)}
+            "GBps": round(sum(alg.values()) / (step_ms * 1e-3) / 1e9, 1),
+            "pre_reduced_combine": {
+                "per_call_us": {ph: round(rtot[ph] / K / len(red[ph]) * 1e3, 2) for ph in rorder},
+                "rows_back": rows_back, "rows_back_without": rows_total,
+                "bytes_back": rows_back * H * b, "bytes_back_without": rows_total * H * b,
+                "bytes_saved_frac": round(1 - rows_back / rows_total, 4),
+                "vs_receiver_only_max_bf16_codes": int(dist.max().item()),
+                "vs_receiver_only_frac_elements_differing": round(
+                    float((dist > 0).float().mean().item()), 5)}}
 
 
 def main():

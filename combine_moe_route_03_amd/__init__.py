@@ -9,7 +9,8 @@ _EXPORTS = ("moe_route_topk", "moe_dispatch_workspace_bytes", "moe_dispatch_layo
             "moe_dispatch_pack", "moe_dispatch", "moe_route_dispatch", "moe_combine",
             "moe_status_str", "alloc_dispatch_out", "alloc_workspace", "DispatchBuffers",
             "MoeError", "moe_ep_capacity", "moe_ep_send", "moe_ep_recv", "moe_ep_return",
-            "moe_ep_combine")
+            "moe_ep_combine", "moe_ep_partial_rows", "moe_ep_reduce", "moe_ep_reduce_workspace",
+            "moe_ep_combine_reduced")
 
 
 def __getattr__(name):

@@ -63,9 +63,15 @@ def load() -> ctypes.CDLL:
         lib.moe_ep_recv.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P, P, P]
         lib.moe_ep_return.argtypes = [P, I, I, I, I, I, I, P, P, P, P]
         lib.moe_ep_combine.argtypes = [P, I, I, I, I, P, P, I, P, I, P]
+        lib.moe_ep_partial_rows.argtypes = [P, I, I, I, I, I, I, I, P, P, P]
+        lib.moe_ep_reduce_workspace_bytes.argtypes = [I, I]
+        lib.moe_ep_reduce_workspace_bytes.restype = Z
+        lib.moe_ep_reduce.argtypes = [P, I, I, I, I, I, I, I, P, I, I, P, P, P, P, I, P, P, Z, P]
+        lib.moe_ep_combine_reduced.argtypes = [P, I, I, I, I, P, I, P, I, P]
         for fn in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_dispatch",
                    "moe_route_dispatch", "moe_combine", "moe_ep_send", "moe_ep_recv",
-                   "moe_ep_return", "moe_ep_combine"):
+                   "moe_ep_return", "moe_ep_combine", "moe_ep_partial_rows", "moe_ep_reduce",
+                   "moe_ep_combine_reduced"):
             getattr(lib, fn).restype = I
         _lib = lib
     return _lib
@@ -270,4 +276,46 @@ def moe_ep_combine(returns: torch.Tensor, send_row: torch.Tensor, topk_w: torch.
     _check("moe_ep_combine", load().moe_ep_combine(
         _ptr(returns), _dtype_code(returns), T, H, k, _ptr(send_row), _ptr(topk_w),
         returns.shape[0], _ptr(out), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def moe_ep_partial_rows(topk_idx: torch.Tensor, E: int, n_ranks: int, source: int,
+                        n_sources: int, pcap: int, part_row: torch.Tensor,
+                        part_counts: torch.Tensor, stream=None) -> torch.Tensor:
+    """Partial-row layout of one source: part_row [T, N], part_counts column `source`."""
+    T, k = topk_idx.shape
+    _check("moe_ep_partial_rows", load().moe_ep_partial_rows(
+        _ptr(topk_idx), T, k, E, n_ranks, source, n_sources, pcap, _ptr(part_row),
+        _ptr(part_counts), _stream(stream)))
+    return part_row
+
+
+def moe_ep_reduce(y_grouped: torch.Tensor, E: int, n_ranks: int, rank: int, n_sources: int,
+                  cap: int, grouped_src: torch.Tensor, topk_idx: torch.Tensor,
+                  topk_w: torch.Tensor, send_row: torch.Tensor, part_row: torch.Tensor, pcap: int,
+                  partials: torch.Tensor, workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Expert side of the pre-reduced combine for one rank (source tables stacked)."""
+    H = y_grouped.shape[1]
+    TT, k = topk_idx.shape
+    _check("moe_ep_reduce", load().moe_ep_reduce(
+        _ptr(y_grouped), _dtype_code(y_grouped), H, E, n_ranks, rank, n_sources, cap,
+        _ptr(grouped_src), TT // n_sources, k, _ptr(topk_idx), _ptr(topk_w), _ptr(send_row),
+        _ptr(part_row), pcap, _ptr(partials), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return partials
+
+
+def moe_ep_reduce_workspace(n_sources: int, cap: int, device="cuda") -> torch.Tensor:
+    n = max(int(load().moe_ep_reduce_workspace_bytes(n_sources, cap)), 1)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_ep_combine_reduced(partials: torch.Tensor, part_row: torch.Tensor, out: torch.Tensor,
+                           stream=None) -> torch.Tensor:
+    """Source side of the pre-reduced combine: a token's partial rows added in rank order."""
+    T, N = part_row.shape
+    H = partials.shape[1]
+    _check("moe_ep_combine_reduced", load().moe_ep_combine_reduced(
+        _ptr(partials), _dtype_code(partials), T, H, N, _ptr(part_row), partials.shape[0],
+        _ptr(out), _dtype_code(out), _stream(stream)))
     return out

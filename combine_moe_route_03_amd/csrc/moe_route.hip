@@ -30,7 +30,9 @@
 //   k_ep_recv_plan   expert-parallel receive: one workgroup turns a rank's per-(source, expert)
 //                    region counts into the grouped layout and each grouped row's region row;
 //   k_copy_rows      grid-stride row gather / scatter by a row map (expert-parallel receive and
-//                    the return half of combine).
+//                    the return half of combine);
+//   k_ep_partial_rows, k_ep_invert, k_ep_reduce, k_ep_finish  combine with pre-reduction on the
+//                    expert side: one partial row per (token, rank), summed by the source.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -1107,6 +1109,130 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_combine(
     Store8<OT>::run(out + t * H + off, acc);
 }
 
+
+// ------------------------------------------------------------ combine with pre-reduction (EP) --
+// Where the partial rows of one source go: workgroup r scans the source's tokens in order, 1024 at
+// a time; token t takes row (r*S + source)*pcap + p when one of its experts sits on rank r (p
+// counts such tokens before t), else -1. part_counts[r*S + source] = the number of such tokens.
+__global__ __launch_bounds__(kGroupThreads) void k_ep_partial_rows(
+    const int32_t* __restrict__ topk_idx, int32_t T, int32_t k, int32_t L, int32_t S,
+    int32_t source, int32_t pcap, int32_t N, int32_t* __restrict__ part_row,
+    int32_t* __restrict__ part_counts)
+{
+    __shared__ uint32_t wave_tot[kGroupWaves];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    uint32_t base = 0u;
+    for (int t0 = 0; t0 < T; t0 += kGroupThreads) {     // uniform across the workgroup
+        const int t = t0 + tid;
+        uint32_t on = 0u;
+        if (t < T)
+            for (int j = 0; j < k; ++j)
+                on |= (topk_idx[(int64_t)t * k + j] / L == r) ? 1u : 0u;
+        uint32_t n = 0u;
+        const uint32_t before = block_exclusive_scan<kGroupThreads>(on, wave_tot, &n);
+        if (t < T)
+            part_row[(int64_t)t * N + r] =
+                on ? (int32_t)(((int64_t)r * S + source) * pcap + base + before) : -1;
+        base += n;
+        __syncthreads();                                 // wave_tot is reused next round
+    }
+    if (tid == 0)
+        part_counts[(int64_t)r * S + source] = (int32_t)base;
+}
+
+// Grouped row of every region row of one rank: inv[grouped_src[g] - base] = g.
+__global__ __launch_bounds__(kThreads) void k_ep_invert(const int32_t* __restrict__ grouped_src,
+                                                        int64_t n, int64_t base,
+                                                        int32_t* __restrict__ inv)
+{
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n;
+         g += (int64_t)gridDim.x * kThreads) {
+        const int64_t q = (int64_t)grouped_src[g] - base;
+        if (grouped_src[g] >= 0 && q >= 0 && q < n)
+            inv[q] = (int32_t)g;
+    }
+}
+
+// Expert side: one wavefront per (token of any source, 512-element segment). Lanes j < k read
+// the token's slots; the slots whose expert sits on this rank are added in slot order, fp32
+// multiply-adds of w * y[grouped row], and the sum is rounded once into the token's partial row.
+template <typename YT>
+__global__ __launch_bounds__(64 * kCombineWaves) void k_ep_reduce(
+    const YT* __restrict__ y, int32_t H, int32_t nseg, int64_t tokens, int32_t k, int32_t L,
+    int32_t N, int32_t rank, int64_t base, int64_t nreg, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ send_row,
+    const int32_t* __restrict__ part_row, const int32_t* __restrict__ inv, int64_t part_limit,
+    YT* __restrict__ partials)
+{
+    const int64_t item = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+    const int64_t tt = item / nseg;
+    if (tt >= tokens)
+        return;
+    const int32_t pr = part_row[tt * N + rank];
+    if (pr < 0 || (int64_t)pr >= part_limit)
+        return;                                          // uniform per wavefront
+    const int lane = threadIdx.x & 63;
+    int32_t g_mine = -1;
+    float w_mine = 0.0f;
+    if (lane < k && topk_idx[tt * k + lane] / L == rank) {
+        const int64_t q = (int64_t)send_row[tt * k + lane] - base;
+        g_mine = (q >= 0 && q < nreg) ? inv[q] : -1;
+        if (g_mine >= nreg)
+            g_mine = -1;                                 // never outside the grouped rows
+        w_mine = topk_w[tt * k + lane];
+    }
+    const int seg = (int)(item - tt * nseg);
+    const int c = seg * 64 + lane;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] = 0.0f;
+    const bool active = c < H / 8;
+    for (int j = 0; j < k; ++j) {
+        const int32_t g = __builtin_amdgcn_readlane(g_mine, j);
+        if (g < 0)
+            continue;                                    // uniform per wavefront
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_mine), j));
+        if (active) {
+            Y8<YT> v;
+            v.load(y + (int64_t)g * H + (int64_t)c * 8);
+            v.fma_into(wj, acc);
+        }
+    }
+    if (active)
+        Store8<YT>::run(partials + (int64_t)pr * H + (int64_t)c * 8, acc);
+}
+
+// Source side: one wavefront per (token, 512-element segment); the token's partial rows are added
+// in rank order in fp32 and the sum is rounded once.
+template <typename YT, typename OT>
+__global__ __launch_bounds__(64 * kCombineWaves) void k_ep_finish(
+    const YT* __restrict__ partials, int32_t T, int32_t H, int32_t nseg, int32_t N,
+    const int32_t* __restrict__ part_row, int64_t part_limit, OT* __restrict__ out)
+{
+    const int64_t item = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+    const int64_t t = item / nseg;
+    if (t >= T)
+        return;
+    const int seg = (int)(item - t * nseg);
+    const int c = seg * 64 + (threadIdx.x & 63);
+    if (c >= H / 8)
+        return;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] = 0.0f;
+    for (int r = 0; r < N; ++r) {
+        const int32_t pr = part_row[t * N + r];
+        if (pr < 0 || (int64_t)pr >= part_limit)
+            continue;
+        Y8<YT> v;
+        v.load(partials + (int64_t)pr * H + (int64_t)c * 8);
+        v.fma_into(1.0f, acc);
+    }
+    Store8<OT>::run(out + t * H + (int64_t)c * 8, acc);
+}
+
 // ------------------------------------------------------------------------------ host helpers --
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -1789,6 +1915,112 @@ moe_status_t moe_ep_return(const void* y_grouped, moe_dtype_t dtype, int32_t H, 
     launch_copy_rows(COPY_SCATTER, y_grouped, returns, dtype, H, grouped_src,
                      expert_offsets + E / n_ranks, (int64_t)n_sources * cap,
                      (int64_t)n_ranks * n_sources * cap, stream);
+    return launch_status();
+}
+
+moe_status_t moe_ep_partial_rows(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                 int32_t n_ranks, int32_t source, int32_t n_sources, int32_t pcap,
+                                 int32_t* part_row, int32_t* part_counts, hipStream_t stream)
+{
+    moe_status_t st = ep_region_args(E, n_ranks, n_sources, pcap);
+    if (st != MOE_OK)
+        return st;
+    if (T < 0 || k < 1 || pcap < T || source < 0 || source >= n_sources ||
+        (int64_t)T * n_ranks > INT32_MAX || (int64_t)T * k > INT32_MAX)
+        return MOE_ERR_INVALID;
+    if (!part_counts || (T > 0 && (!topk_idx || !part_row)))
+        return MOE_ERR_INVALID;
+    k_ep_partial_rows<<<(unsigned)n_ranks, kGroupThreads, 0, stream>>>(
+        topk_idx, T, k, E / n_ranks, n_sources, source, pcap, n_ranks, part_row, part_counts);
+    return launch_status();
+}
+
+size_t moe_ep_reduce_workspace_bytes(int32_t n_sources, int32_t cap)
+{
+    if (n_sources < 1 || cap < 0)
+        return 0;
+    return align_up((size_t)n_sources * (size_t)(cap > 0 ? cap : 1) * sizeof(int32_t), 256);
+}
+
+moe_status_t moe_ep_reduce(const void* y_grouped, moe_dtype_t dtype, int32_t H, int32_t E,
+                           int32_t n_ranks, int32_t rank, int32_t n_sources, int32_t cap,
+                           const int32_t* grouped_src, int32_t T, int32_t k,
+                           const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,
+                           const int32_t* part_row, int32_t pcap, void* partials, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream)
+{
+    moe_status_t st = ep_rank_args(dtype, H, E, n_ranks, n_sources, cap, y_grouped, partials);
+    if (st != MOE_OK)
+        return st;
+    st = ep_region_args(E, n_ranks, n_sources, pcap);
+    if (st != MOE_OK)
+        return st;
+    if (rank < 0 || rank >= n_ranks || T < 0 || k < 1 || pcap < T ||
+        (int64_t)n_sources * T * (k > n_ranks ? k : n_ranks) > INT32_MAX)
+        return MOE_ERR_INVALID;
+    if (H % 8 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t tokens = (int64_t)n_sources * T;
+    if (tokens == 0 || cap == 0)
+        return MOE_OK;
+    if (!y_grouped || !grouped_src || !topk_idx || !topk_w || !send_row || !part_row ||
+        !partials)
+        return MOE_ERR_INVALID;
+    if (!workspace || workspace_bytes < moe_ep_reduce_workspace_bytes(n_sources, cap))
+        return MOE_ERR_WORKSPACE;
+    int32_t* inv = static_cast<int32_t*>(workspace);
+    const int64_t nreg = (int64_t)n_sources * cap;
+    const int64_t base = (int64_t)rank * nreg;
+    int64_t blocks = ceil_div(nreg, kThreads);
+    blocks = blocks > 4096 ? 4096 : blocks;
+    k_ep_invert<<<(unsigned)blocks, kThreads, 0, stream>>>(grouped_src, nreg, base, inv);
+    const int32_t nseg = (int32_t)ceil_div(H / 8, 64);
+    const dim3 grid((unsigned)ceil_div(tokens * nseg, kCombineWaves));
+    const int64_t part_limit = (int64_t)n_ranks * n_sources * pcap;
+    if (dtype == MOE_BF16)
+        k_ep_reduce<uint16_t><<<grid, 64 * kCombineWaves, 0, stream>>>(
+            static_cast<const uint16_t*>(y_grouped), H, nseg, tokens, k, E / n_ranks, n_ranks,
+            rank, base, nreg, topk_idx, topk_w, send_row, part_row, inv, part_limit,
+            static_cast<uint16_t*>(partials));
+    else
+        k_ep_reduce<float><<<grid, 64 * kCombineWaves, 0, stream>>>(
+            static_cast<const float*>(y_grouped), H, nseg, tokens, k, E / n_ranks, n_ranks, rank,
+            base, nreg, topk_idx, topk_w, send_row, part_row, inv, part_limit,
+            static_cast<float*>(partials));
+    return launch_status();
+}
+
+moe_status_t moe_ep_combine_reduced(const void* partials, moe_dtype_t dtype, int32_t T, int32_t H,
+                                    int32_t n_ranks, const int32_t* part_row,
+                                    int32_t partial_rows, void* out, moe_dtype_t out_dtype,
+                                    hipStream_t stream)
+{
+    if (T < 0 || H < 1 || n_ranks < 1 || partial_rows < 0 || (int64_t)T * n_ranks > INT32_MAX)
+        return MOE_ERR_INVALID;
+    if (!is_wide(dtype) || !is_wide(out_dtype) || H % 8 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if (T > 0 && (!partials || !part_row || !out))
+        return MOE_ERR_INVALID;
+    if (!aligned(partials, 16) || !aligned(out, 16))
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_OK;
+    const int32_t nseg = (int32_t)ceil_div(H / 8, 64);
+    const dim3 grid((unsigned)ceil_div((int64_t)T * nseg, kCombineWaves));
+    const dim3 block(64 * kCombineWaves);
+#define MOE_FINISH(YT, OT)                                                                        \
+    k_ep_finish<YT, OT><<<grid, block, 0, stream>>>(static_cast<const YT*>(partials), T, H, nseg,  \
+                                                    n_ranks, part_row, partial_rows,             \
+                                                    static_cast<OT*>(out))
+    if (dtype == MOE_BF16 && out_dtype == MOE_BF16)
+        MOE_FINISH(uint16_t, uint16_t);
+    else if (dtype == MOE_BF16)
+        MOE_FINISH(uint16_t, float);
+    else if (out_dtype == MOE_BF16)
+        MOE_FINISH(float, uint16_t);
+    else
+        MOE_FINISH(float, float);
+#undef MOE_FINISH
     return launch_status();
 }
 

@@ -234,6 +234,52 @@ moe_status_t moe_ep_combine(const void* returns, moe_dtype_t y_dtype, int32_t T,
                             int32_t region_rows, void* out, moe_dtype_t out_dtype,
                             hipStream_t stream);
 
+/*
+ * Combine with pre-reduction on the expert side. The pages accumulate only on the receiver and
+ * name that as the reason they lag at prefill ("Evaluatie / Dispatch/Combine-latentie"). Here rank
+ * r first sums, for every token that has experts on r, the weighted outputs of those experts into
+ * one partial row (fp32 multiply-adds in slot order, rounded once to the partial format); only the
+ * partial rows travel back, and the source adds a token's partial rows in rank order (fp32,
+ * rounded once). One row per (token, rank) instead of one per (token, slot) travels back, at the
+ * cost of a second rounding.
+ *   - Partial array [N*S*pcap, H], pcap >= T: the partial rows of (rank r, source s) sit at rows
+ *     [(r*S + s)*pcap, ...) in token order; part_row [T, N] of a source names the row of (t, r),
+ *     -1 when t has no expert on r.
+ */
+
+/* Partial-row layout of source `source`: part_row [T, N] and part_counts[r*S + source] (the rows
+ * it receives from rank r). */
+moe_status_t moe_ep_partial_rows(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                 int32_t n_ranks, int32_t source, int32_t n_sources, int32_t pcap,
+                                 int32_t* part_row, int32_t* part_counts, hipStream_t stream);
+
+/* Bytes of workspace moe_ep_reduce needs (the grouped row of every region row of the rank). */
+size_t moe_ep_reduce_workspace_bytes(int32_t n_sources, int32_t cap);
+
+/*
+ * moe_ep_reduce -- expert side: the partial rows that rank `rank` returns to every source.
+ *   y_grouped [S*cap, H] expert outputs in the rank's grouped layout, grouped_src from
+ *   moe_ep_recv; topk_idx / topk_w [S*T, k], send_row [S*T*k] and part_row [S*T, N] are the
+ *   sources' tables stacked (source s owns tokens [s*T, (s+1)*T)); in a deployment they travel
+ *   with the dispatched rows. Writes partials[part_row[(s*T + t)*N + rank], :] for every token with
+ *   experts on the rank. H % 8 == 0.
+ */
+moe_status_t moe_ep_reduce(const void* y_grouped, moe_dtype_t dtype, int32_t H, int32_t E,
+                           int32_t n_ranks, int32_t rank, int32_t n_sources, int32_t cap,
+                           const int32_t* grouped_src, int32_t T, int32_t k,
+                           const int32_t* topk_idx, const float* topk_w, const int32_t* send_row,
+                           const int32_t* part_row, int32_t pcap, void* partials, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_ep_combine_reduced -- source side: out[t, :] = sum over r of partials[part_row[t*N + r], :]
+ * (rows with part_row -1 or outside [0, partial_rows) skipped), fp32 in rank order, rounded once.
+ */
+moe_status_t moe_ep_combine_reduced(const void* partials, moe_dtype_t dtype, int32_t T, int32_t H,
+                                    int32_t n_ranks, const int32_t* part_row,
+                                    int32_t partial_rows, void* out, moe_dtype_t out_dtype,
+                                    hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_str(moe_status_t status);
 

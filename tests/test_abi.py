@@ -30,7 +30,9 @@ def test_library_loads_and_exports_every_declared_function():
                             "moe_dispatch_pack", "moe_dispatch_workspace_bytes",
                             "moe_route_dispatch", "moe_route_topk", "moe_status_str",
                             "moe_ep_capacity", "moe_ep_send", "moe_ep_recv", "moe_ep_return",
-                            "moe_ep_combine"])
+                            "moe_ep_combine", "moe_ep_partial_rows",
+                            "moe_ep_reduce_workspace_bytes", "moe_ep_reduce",
+                            "moe_ep_combine_reduced"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -216,6 +218,40 @@ def test_ep_capacity_and_validation():
     comb = lib.moe_ep_combine
     assert comb(A16, BF16, 4, 256, 2, A16, A16, -1, A16b, BF16, S0) == moe.MOE_ERR_INVALID
     assert comb(None, BF16, 0, 256, 2, None, None, 0, None, BF16, S0) == moe.MOE_OK
+
+
+def test_ep_reduce_validation():
+    lib = moe.load()
+    BF16, FP8 = moe.MOE_BF16, moe.MOE_FP8_E4M3
+    pr = lib.moe_ep_partial_rows
+    assert pr(A16, 10, 2, 8, 4, 0, 3, 9, A16, A16, S0) == moe.MOE_ERR_INVALID      # pcap < T
+    assert pr(A16, 10, 2, 8, 4, 3, 3, 10, A16, A16, S0) == moe.MOE_ERR_INVALID     # source >= S
+    assert pr(A16, 10, 2, 8, 4, 0, 3, 10, A16, None, S0) == moe.MOE_ERR_INVALID
+    assert lib.moe_ep_reduce_workspace_bytes(3, 20) >= 3 * 20 * 4
+    assert lib.moe_ep_reduce_workspace_bytes(0, 20) == 0
+    red = lib.moe_ep_reduce
+    need = lib.moe_ep_reduce_workspace_bytes(3, 20)
+    ok = dict(y=A16, dt=BF16, H=256, E=8, N=4, rank=1, S=3, cap=20, gs=A16, T=10, k=2, idx=A16,
+              w=A16, row=A16, prow=A16, pcap=10, part=A16b, ws=A16, wsb=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return red(a["y"], a["dt"], a["H"], a["E"], a["N"], a["rank"], a["S"], a["cap"], a["gs"],
+                   a["T"], a["k"], a["idx"], a["w"], a["row"], a["prow"], a["pcap"], a["part"],
+                   a["ws"], a["wsb"], S0)
+
+    assert call(rank=4) == moe.MOE_ERR_INVALID
+    assert call(pcap=9) == moe.MOE_ERR_INVALID
+    assert call(dt=FP8) == moe.MOE_ERR_UNSUPPORTED
+    assert call(H=260) == moe.MOE_ERR_UNSUPPORTED                    # rows of 16 bytes, H % 8
+    assert call(part=MIS) == moe.MOE_ERR_UNSUPPORTED
+    assert call(gs=None) == moe.MOE_ERR_INVALID
+    assert call(wsb=need - 4) == moe.MOE_ERR_WORKSPACE
+    fin = lib.moe_ep_combine_reduced
+    assert fin(A16, BF16, 4, 256, 4, A16, -1, A16b, BF16, S0) == moe.MOE_ERR_INVALID
+    assert fin(A16, FP8, 4, 256, 4, A16, 8, A16b, BF16, S0) == moe.MOE_ERR_UNSUPPORTED
+    assert fin(A16, BF16, 4, 252, 4, A16, 8, A16b, BF16, S0) == moe.MOE_ERR_UNSUPPORTED
+    assert fin(None, BF16, 0, 256, 4, None, 0, None, BF16, S0) == moe.MOE_OK
 
 
 def test_combine_validation():

@@ -90,7 +90,8 @@ def _run(w: EpWorkload, sample_rows: int = 0):
         assert np.array_equal(gs, o_recv[r]["grouped_src"]), f"rank {r} grouped_src differs"
         sel = np.arange(n) if not sample_rows else np.arange(0, n, max(1, n // sample_rows))
         assert np.array_equal(g[sel], o_recv[r]["grouped"][sel]), f"rank {r} grouped rows differ"
-    return x_d, idx_d, recv
+    return dict(x_d=x_d, idx_d=idx_d, w_d=w_d, recv=recv, rows=rows, o_y=o_y, o_recv=o_recv,
+                o_rows=o_rows, idx=idx, wt=wt, o_out=o_out)
 
 
 @pytest.mark.parametrize("name", ["ep_tiny", "ep_decode"])
@@ -111,9 +112,11 @@ def test_ep_grouped_layout_equals_dispatch_of_the_concatenated_batch():
     sources' tokens, rank by rank."""
     w = EpWorkload("ep_mid", 4, 300, 512, 64, 4, 8, "bf16")
     _announce(f"ep grouped == dispatch S={w.S} T={w.T}")
-    x_d, idx_d, recv = _run(w)
+    c = _run(w)
+    recv = c["recv"]
     buf = moe.alloc_dispatch_out(w.S * w.T, w.H, w.E, w.k, w.N, w.dtype)
-    moe.moe_dispatch(x_d, idx_d, w.E, w.N, buf, moe.alloc_workspace(w.S * w.T, w.E, w.k))
+    moe.moe_dispatch(c["x_d"], c["idx_d"], w.E, w.N, buf,
+                     moe.alloc_workspace(w.S * w.T, w.E, w.k))
     torch.cuda.synchronize()
     ro = to_host(buf.rank_offsets)
     d_recv = to_host(buf.recv)
@@ -144,3 +147,62 @@ def test_ep_worst_case_region_is_filled_exactly():
         assert np.array_equal(to_host(row), o_row)
     assert np.array_equal(to_host(counts), o_counts)
     assert np.array_equal(to_host(regions), o_regions)
+
+
+@pytest.mark.parametrize("name", ["ep_tiny", "ep_decode", "ep_mid"])
+def test_ep_combine_with_pre_reduction(name):
+    """Partial-row layout bit-exact; partial rows within one bf16 code (1e-5 for fp32) of the
+    oracle's exact sums; the source-side finish, from the oracle's partial rows, within one code;
+    the whole GPU chain within two codes (a partial one code off moves the output at most one
+    code, since all terms share a sign)."""
+    w = EP_WORKLOADS.get(name) or EpWorkload("ep_mid", 4, 300, 512, 64, 4, 8, "bf16")
+    _announce(f"ep pre-reduced combine {name}")
+    c = _run(w)
+    S, N, T, k = w.S, w.N, w.T, w.k
+    pcap = T
+    # oracle
+    o_pc = np.zeros((N, S), np.int32)
+    o_prow = [oracle.ep_partial_rows(c["idx"][s * T:(s + 1) * T], w.E, N, s, S, pcap, o_pc)
+              for s in range(S)]
+    o_part = np.zeros((N * S * pcap, w.H), oracle.NP_DTYPES[w.dtype])
+    for r in range(N):
+        oracle.ep_reduce(c["o_y"][r], w.dtype, w.E, N, r, S, w.cap, c["o_recv"][r]["grouped_src"],
+                         c["idx"], c["wt"], np.concatenate(c["o_rows"]), np.concatenate(o_prow),
+                         o_part)
+    o_fin = [oracle.ep_combine_reduced(o_part, w.dtype, o_prow[s], w.dtype) for s in range(S)]
+    # GPU
+    tdt = moe.TORCH_DTYPES[w.dtype]
+    pc = torch.full((N, S), -3, dtype=torch.int32, device="cuda")
+    prow = []
+    for s in range(S):
+        p = torch.empty((T, N), dtype=torch.int32, device="cuda")
+        moe.moe_ep_partial_rows(c["idx_d"][s * T:(s + 1) * T], w.E, N, s, S, pcap, p, pc)
+        prow.append(p)
+    prow_all = torch.cat(prow)
+    rows_all = torch.cat(c["rows"])
+    part = torch.zeros((N * S * pcap, w.H), dtype=tdt, device="cuda")
+    ws = moe.moe_ep_reduce_workspace(S, w.cap)
+    for r in range(N):
+        moe.moe_ep_reduce(to_dev(c["o_y"][r], w.dtype), w.E, N, r, S, w.cap, c["recv"][r][3],
+                          c["idx_d"], c["w_d"], rows_all, prow_all, pcap, part, ws)
+    fin = [torch.empty((T, w.H), dtype=tdt, device="cuda") for _ in range(S)]
+    fin_o = [torch.empty((T, w.H), dtype=tdt, device="cuda") for _ in range(S)]
+    part_o = to_dev(o_part, w.dtype)
+    for s in range(S):
+        moe.moe_ep_combine_reduced(part, prow[s], fin[s])
+        moe.moe_ep_combine_reduced(part_o, prow[s], fin_o[s])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(pc), o_pc)
+    g_part = to_host(part)
+    for s in range(S):
+        assert np.array_equal(to_host(prow[s]), o_prow[s])
+        valid = o_prow[s][o_prow[s] >= 0]
+        assert_close_out(g_part[valid], o_part[valid], w.dtype)
+        assert_close_out(to_host(fin_o[s]), o_fin[s], w.dtype)
+        got, want = to_host(fin[s]), o_fin[s]
+        if w.dtype == "bf16":
+            from gpu_util import bf16_ulp_distance
+            assert bf16_ulp_distance(got, want).max() <= 2
+        else:
+            assert_close_out(got, want, w.dtype)
+    assert o_pc.sum() < S * T * k                                   # fewer rows travel back

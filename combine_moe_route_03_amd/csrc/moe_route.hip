@@ -45,10 +45,12 @@ constexpr int kThreads = 256;            // route / histogram workgroups: 4 wave
 constexpr int kWaves = kThreads / 64;
 constexpr int kGroupThreads = 1024;      // 16-wavefront workgroups (route-layout, totals, scan)
 constexpr int kGroupWaves = kGroupThreads / 64;
-constexpr int kRouteTokens = kGroupWaves;   // tokens per route-layout workgroup (one per wave)
+constexpr int kRouteTokens = kGroupWaves;   // route-layout workgroup, k > 16: a token a wave
+constexpr int kRouteTokens16 = kThreads / 16;   // route-layout workgroup, k <= 16: 16 lanes each
+constexpr int kSmallRound = kGroupThreads / 16; // tokens routed at once by the one-workgroup path
 constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
-constexpr int kSmallTokens = 32;         // small batches: routing and layout in one workgroup
-constexpr int kSmallItems = 2048;        //   (T <= 32 tokens, at most 2 per wavefront)
+constexpr int kSmallTokens = 64;         // small batches: routing and layout in one workgroup
+constexpr int kSmallItems = 2048;        //   (T <= 64 tokens, k <= 16, T*k <= 2048)
 constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
 constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
 constexpr int kCombineWaves = 2;         // wavefronts per combine workgroup
@@ -310,8 +312,9 @@ __device__ __forceinline__ int route_token(const float* __restrict__ l, int32_t 
     return route_token_from<PL>(v, E, k, idx_out, w_out);
 }
 
+// Routing with one whole wavefront per token (any k up to 64).
 template <int PL>
-__global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(kThreads) void k_route_topk_wide(const float* __restrict__ logits,
                                                          int32_t T, int32_t E, int32_t k,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w)
@@ -322,14 +325,15 @@ __global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict
     route_token<PL>(logits + t * E, E, k, topk_idx + t * k, topk_w + t * k);
 }
 
-// Routing plus the counting half of dispatch in one launch. Workgroup b routes tokens
+// Routing plus the counting half of dispatch in one launch, one wavefront per token (used for
+// k > 16). Workgroup b routes tokens
 // 16b .. 16b+15 (wavefront w takes token 16b + w); each selected (token, slot) sets bit w of
 // the LDS mask of its expert. A token's k experts are distinct, so the rank of (token, slot)
 // among the workgroup's items of the same expert, in (token, slot) order, is the number of bits
 // below w, and the workgroup's count of expert e is popcount(mask[e]), stored block-major at
 // hist[b * E + e] (one coalesced row per workgroup). LDS: mask [E] u32.
 template <int PL>
-__global__ __launch_bounds__(kGroupThreads) void k_route_layout(
+__global__ __launch_bounds__(kGroupThreads) void k_route_layout_wide(
     const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ hist,
     uint32_t* __restrict__ local_rank)
@@ -351,6 +355,165 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_layout(
         local_rank[t * k + lane] = (uint32_t)__popc(lds_mask[my_id] & ((1u << wave) - 1u));
     for (int e = tid; e < E; e += kGroupThreads)
         hist[(int64_t)blockIdx.x * E + e] = (uint32_t)__popc(lds_mask[e]);
+}
+
+// ------------------------------------------------------------------ routing, 16 lanes a token --
+// For k <= 16 a wavefront routes 4 tokens at once, one per 16-lane DPP row, which takes about a
+// third of the instructions per token of the wavefront-per-token selection (routing is bound by
+// issue: 4096 tokens give every SIMD only a few wavefronts).
+__device__ __forceinline__ uint32_t logit_key(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u)
+        u = 0u;                                          // -0 equals +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // every finite logit maps above 0
+}
+
+__device__ __forceinline__ float key_logit(uint32_t ord)
+{
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<kDppQuadXor1>(v));
+    v = max(v, dpp_u32<kDppQuadXor2>(v));
+    v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+    return max(v, dpp_u32<kDppRowMirror>(v));
+}
+
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t v)
+{
+    v = min(v, dpp_u32<kDppQuadXor1>(v));
+    v = min(v, dpp_u32<kDppQuadXor2>(v));
+    v = min(v, dpp_u32<kDppRowHalfMirror>(v));
+    return min(v, dpp_u32<kDppRowMirror>(v));
+}
+
+// The logits of a row's token: lane l of the row holds experts l, l+16, ... (entries past `E`
+// are not read; a row with E = 0 routes nothing).
+template <int P>
+__device__ __forceinline__ void load_logits16(const float* __restrict__ l, int32_t E,
+                                              float (&v)[P])
+{
+    const int l16 = threadIdx.x & 15;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int e = l16 + 16 * p;
+        v[p] = (e < E) ? l[e] : 0.0f;
+    }
+}
+
+// Top-k of the token of each 16-lane row (all lanes active, k <= 16). Each lane keeps its keys
+// (0 marks an expert taken or absent) and its best remaining one: the largest key, the lowest
+// expert among equal keys of the lane. Round j takes the row's largest key and, among the lanes
+// holding it, the lowest expert id (two DPP reductions inside the row), so the winner is the
+// largest logit with ties to the lower id; its owner clears the key and rescans. Lane j < k of the
+// row keeps slot j; `valid` = false (a row past the last token) routes nothing and writes
+// nothing. The weights use double-precision exp and division, rounded once to fp32. Returns the
+// lane's expert id for lanes j < k of a valid row, else -1.
+template <int P>
+__device__ __forceinline__ int route_row16(const float (&v)[P], int32_t E, int32_t k, bool valid,
+                                           int32_t* __restrict__ idx_out,
+                                           float* __restrict__ w_out)
+{
+    const int l16 = threadIdx.x & 15;
+    uint32_t key[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        key[p] = (valid && l16 + 16 * p < E) ? logit_key(v[p]) : 0u;
+    uint32_t bk = 0u;
+    int bp = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (key[p] > bk) {
+            bk = key[p];
+            bp = p;
+        }
+    int my_id = -1;
+    uint32_t my_key = 0u, top_key = 0u;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t m = row16_max_u32(bk);
+        const uint32_t mine = (uint32_t)(l16 + 16 * bp);
+        const uint32_t cand = row16_min_u32((m != 0u && bk == m) ? mine : 0xFFFFFFFFu);
+        if (j == 0)
+            top_key = m;
+        if (l16 == j && m != 0u) {
+            my_id = (int)cand;
+            my_key = m;
+        }
+        if (m != 0u && bk == m && mine == cand) {      // the owner clears its key and rescans
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                key[p] = (p == bp) ? 0u : key[p];
+            bk = 0u;
+            bp = 0;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                if (key[p] > bk) {
+                    bk = key[p];
+                    bp = p;
+                }
+        }
+    }
+    const bool slot = valid && l16 < k;
+    double ex = slot ? exp((double)key_logit(my_key) - (double)key_logit(top_key)) : 0.0;
+    double sum = ex;
+    sum = dpp_add_f64<kDppQuadXor1>(sum);
+    sum = dpp_add_f64<kDppQuadXor2>(sum);
+    sum = dpp_add_f64<kDppRowHalfMirror>(sum);
+    sum = dpp_add_f64<kDppRowMirror>(sum);
+    if (slot) {
+        idx_out[l16] = my_id;
+        w_out[l16] = (float)(ex / sum);
+    }
+    return slot ? my_id : -1;
+}
+
+// Routing only, 16 lanes a token: 4 tokens per wavefront, 16 per workgroup.
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_route_topk(const float* __restrict__ logits,
+                                                         int32_t T, int32_t E, int32_t k,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w)
+{
+    const int64_t t = (int64_t)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
+    const bool valid = t < T;
+    float v[P];
+    load_logits16<P>(logits + (valid ? t : 0) * E, valid ? E : 0, v);
+    route_row16<P>(v, E, k, valid, topk_idx + t * k, topk_w + t * k);
+}
+
+// Routing plus the counting half of dispatch, 16 lanes a token (k <= 16). Workgroup b (4
+// wavefronts) routes tokens 16b .. 16b+15 (token q of the block in row q % 4 of wavefront q / 4);
+// each selected (token, slot) sets bit q of the LDS mask of its expert. A token's k experts are
+// distinct, so the rank of (token, slot) among the block's items of the same expert, in (token,
+// slot) order, is the number of mask bits below q, and the block's count of expert e is
+// popcount(mask[e]), stored block-major at hist[b * E + e]. LDS: mask [E] u32.
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_route_layout(
+    const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ hist,
+    uint32_t* __restrict__ local_rank)
+{
+    extern __shared__ uint32_t lds_mask32[];
+    const int tid = threadIdx.x, l16 = tid & 15;
+    const int q = tid >> 4;                              // token of the block, 0..15
+    for (int e = tid; e < E; e += kThreads)
+        lds_mask32[e] = 0u;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kRouteTokens16 + q;
+    const bool valid = t < T;
+    float v[P];
+    load_logits16<P>(logits + (valid ? t : 0) * E, valid ? E : 0, v);
+    const int my_id = route_row16<P>(v, E, k, valid, topk_idx + t * k, topk_w + t * k);
+    if (my_id >= 0)
+        atomicOr(&lds_mask32[my_id], 1u << q);
+    __syncthreads();
+    if (my_id >= 0)
+        local_rank[t * k + l16] = (uint32_t)__popc(lds_mask32[my_id] & ((1u << q) - 1u));
+    for (int e = tid; e < E; e += kThreads)
+        hist[(int64_t)blockIdx.x * E + e] = (uint32_t)__popc(lds_mask32[e]);
 }
 
 // --------------------------------------------------------------------------------- layout --
@@ -594,16 +757,17 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
         rp.list[i] = make_int2(-1, -1);
 }
 
-// Routing and the whole layout of a small batch (T <= kSmallTokens, T*k <= kSmallItems) in one
-// workgroup of 16 wavefronts, with no step between workgroups. Wavefront w routes tokens w, w+16,
-// ... (loading the next token's logits before routing the current one); the expert ids stay in LDS
-// and LDS counters count the experts. One block scan gives the expert offsets and the count
-// outputs. Then the tokens are taken 16 at a time, in order: token 16c + w sets bit w in the LDS
-// masks of its experts, and item (t, j) with expert e takes row
-// eoff[e] + run[e] + popcount(mask[e] & bits below w); run[e] then advances by popcount(mask[e]).
+// Routing and the whole layout of a small batch (T <= kSmallTokens, k <= 16, T*k <= kSmallItems)
+// in one workgroup, with no step between workgroups. Tokens are routed 64 at a time, 16 lanes a
+// token (the next round's logits are loaded before the current round is routed; one round is the
+// whole batch at the current limit, and routing is bound by this one CU's issue rate); the ids
+// stay in LDS and LDS counters count the experts. One block scan gives the expert offsets and the
+// count outputs. Then the tokens are taken 64 at a time, in order: token 64c + q sets bit q in the
+// LDS masks of its experts, and item (t, j) with expert e takes row
+// eoff[e] + run[e] + popcount(mask[e] & bits below q); run[e] then advances by popcount(mask[e]).
 // Routed ids are distinct within a token, so this is the stable (expert, token, slot) order.
-// LDS: ids [kSmallItems] u16, count/run [E], offsets [E + 1], masks [E] u32.
-template <int PL>
+// LDS: ids [kSmallItems] u16, count/run [E] u32, offsets [E + 1] u32, masks [E] u64.
+template <int P>
 __global__ __launch_bounds__(kGroupThreads) void k_route_layout_small(
     const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ token_row,
@@ -612,32 +776,33 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_layout_small(
     __shared__ uint16_t ids[kSmallItems];
     __shared__ uint32_t run[MOE_MAX_EXPERTS];
     __shared__ uint32_t eoff[MOE_MAX_EXPERTS + 1];
-    __shared__ uint32_t mask[MOE_MAX_EXPERTS];
+    __shared__ uint64_t mask[MOE_MAX_EXPERTS];
     __shared__ uint32_t wave_tot[kGroupWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, l16 = tid & 15;
+    const int q = tid >> 4;                              // token of the round, 0..63
     for (int e = tid; e < E; e += kGroupThreads) {
         run[e] = 0u;
-        mask[e] = 0u;
+        mask[e] = 0ull;
     }
     __syncthreads();
-    float cur[PL], nxt[PL];
+    float cur[P], nxt[P];
 #pragma unroll
-    for (int p = 0; p < PL; ++p)
+    for (int p = 0; p < P; ++p)
         nxt[p] = 0.0f;
-    if (wave < T)
-        load_logits<PL>(logits + (int64_t)wave * E, E, cur);
-    for (int t = wave; t < T; t += kGroupWaves) {       // uniform per wavefront
-        const int tn = t + kGroupWaves;
+    load_logits16<P>(logits + (int64_t)(q < T ? q : 0) * E, q < T ? E : 0, cur);
+    for (int c0 = 0; c0 < T; c0 += kSmallRound) {   // uniform across the workgroup
+        const int t = c0 + q;
+        const int tn = t + kSmallRound;
         if (tn < T)
-            load_logits<PL>(logits + (int64_t)tn * E, E, nxt);
-        const int id = route_token_from<PL>(cur, E, k, topk_idx + (int64_t)t * k,
-                                            topk_w + (int64_t)t * k);
+            load_logits16<P>(logits + (int64_t)tn * E, E, nxt);
+        const int id = route_row16<P>(cur, E, k, t < T, topk_idx + (int64_t)t * k,
+                                      topk_w + (int64_t)t * k);
         if (id >= 0) {
-            ids[t * k + lane] = (uint16_t)id;
+            ids[t * k + l16] = (uint16_t)id;
             atomicAdd(&run[id], 1u);
         }
 #pragma unroll
-        for (int p = 0; p < PL; ++p)
+        for (int p = 0; p < P; ++p)
             cur[p] = nxt[p];
     }
     __syncthreads();
@@ -664,24 +829,25 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_layout_small(
         co.expert_offsets[E] = (int32_t)total;
         co.rank_offsets[co.N] = (int32_t)total;
     }
-    for (int c0 = 0; c0 < T; c0 += kGroupWaves) {      // uniform across the workgroup
-        const int t = c0 + wave;
-        const bool mine_item = t < T && lane < k;
-        const int e = mine_item ? (int)ids[t * k + lane] : 0;
+    for (int c0 = 0; c0 < T; c0 += kSmallRound) {   // uniform across the workgroup
+        const int t = c0 + q;
+        const bool mine_item = t < T && l16 < k;
+        const int e = mine_item ? (int)ids[t * k + l16] : 0;
         if (mine_item)
-            atomicOr(&mask[e], 1u << wave);
+            atomicOr((unsigned long long*)&mask[e], 1ull << q);
         __syncthreads();
         if (mine_item) {
-            const uint32_t row = eoff[e] + run[e] + (uint32_t)__popc(mask[e] & ((1u << wave) - 1u));
-            token_row[t * k + lane] = (int32_t)row;
+            const uint32_t row =
+                eoff[e] + run[e] + (uint32_t)__popcll(mask[e] & ((1ull << q) - 1ull));
+            token_row[t * k + l16] = (int32_t)row;
             row_token[row] = t;
         }
         __syncthreads();
         for (int ee = tid; ee < E; ee += kGroupThreads) {
-            const uint32_t m = mask[ee];
-            if (m != 0u) {
-                run[ee] += (uint32_t)__popc(m);
-                mask[ee] = 0u;
+            const uint64_t m = mask[ee];
+            if (m != 0ull) {
+                run[ee] += (uint32_t)__popcll(m);
+                mask[ee] = 0ull;
             }
         }
         __syncthreads();
@@ -1260,13 +1426,23 @@ inline LayoutPlan hist_plan(int64_t R)
     return p;
 }
 
-inline bool fused_route_fits(int32_t T) { return T <= kMaxScanBlocks * kRouteTokens; }
+// Tokens per routing-and-counting workgroup: 16 either way (4 wavefronts of 4 tokens for k <= 16,
+// 16 wavefronts of one token otherwise). Below 1024 tokens routing is bound by the latency of one
+// selection, not by issue, and the wavefront-per-token kernels finish sooner.
+inline bool route_rows16(int32_t T, int32_t k) { return k <= 16 && T >= 1024; }
+
+inline int32_t route_block_tokens(int32_t k) { return k <= 16 ? kRouteTokens16 : kRouteTokens; }
+
+inline bool fused_route_fits(int32_t T, int32_t k)
+{
+    return ceil_div(T, route_block_tokens(k)) <= kMaxScanBlocks;
+}
 
 inline LayoutPlan route_plan(int32_t T, int32_t k)
 {
     LayoutPlan p;
-    p.rows_per_block = kRouteTokens * k;
-    p.nblk = (int32_t)ceil_div(T, kRouteTokens);
+    p.rows_per_block = route_block_tokens(k) * k;
+    p.nblk = (int32_t)ceil_div(T, route_block_tokens(k));
     return p;
 }
 
@@ -1289,7 +1465,7 @@ struct Workspace {
 inline int64_t ws_nblk(int32_t T, int32_t k)
 {
     int64_t n = hist_plan((int64_t)T * k).nblk;
-    if (fused_route_fits(T) && route_plan(T, k).nblk > n)
+    if (fused_route_fits(T, k) && route_plan(T, k).nblk > n)
         n = route_plan(T, k).nblk;
     return n;
 }
@@ -1435,11 +1611,41 @@ moe_status_t check_route_args(const float* logits, int32_t T, int32_t E, int32_t
             KERNEL<16><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                \
     } while (0)
 
+// 16 lanes a token: P = ceil(E / 16) keys a lane, rounded up to an instantiated width.
+#define MOE_ROUTE16_LAUNCH(KERNEL, GRID, BLOCK, LDS, ...)                                        \
+    do {                                                                                          \
+        const int p16_ = (int)ceil_div(E, 16);                                                    \
+        if (p16_ <= 1)                                                                            \
+            KERNEL<1><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (p16_ <= 2)                                                                       \
+            KERNEL<2><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (p16_ <= 4)                                                                       \
+            KERNEL<4><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (p16_ <= 8)                                                                       \
+            KERNEL<8><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                 \
+        else if (p16_ <= 16)                                                                      \
+            KERNEL<16><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                \
+        else if (p16_ <= 24)                                                                      \
+            KERNEL<24><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                \
+        else if (p16_ <= 32)                                                                      \
+            KERNEL<32><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                \
+        else if (p16_ <= 48)                                                                      \
+            KERNEL<48><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                \
+        else                                                                                      \
+            KERNEL<64><<<GRID, BLOCK, LDS, stream>>>(__VA_ARGS__);                                \
+    } while (0)
+
 void launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
                   float* topk_w, hipStream_t stream)
 {
-    const dim3 grid((unsigned)ceil_div(T, kWaves));
-    MOE_ROUTE_LAUNCH(k_route_topk, grid, kThreads, 0, logits, T, E, k, topk_idx, topk_w);
+    if (route_rows16(T, k)) {
+        const dim3 grid((unsigned)ceil_div(T, kThreads / 16));
+        MOE_ROUTE16_LAUNCH(k_route_topk, grid, kThreads, 0, logits, T, E, k, topk_idx, topk_w);
+    } else {
+        const dim3 grid((unsigned)ceil_div(T, kWaves));
+        MOE_ROUTE_LAUNCH(k_route_topk_wide, grid, kThreads, 0, logits, T, E, k, topk_idx,
+                         topk_w);
+    }
 }
 
 void launch_route_layout(const float* logits, int32_t T, int32_t E, int32_t k,
@@ -1447,9 +1653,12 @@ void launch_route_layout(const float* logits, int32_t T, int32_t E, int32_t k,
                          const LayoutPlan& plan, hipStream_t stream)
 {
     const dim3 grid((unsigned)plan.nblk);
-    const size_t lds = (size_t)E * sizeof(uint32_t);
-    MOE_ROUTE_LAUNCH(k_route_layout, grid, kGroupThreads, lds, logits, T, E, k, topk_idx, topk_w,
-                     ws.hist, ws.local_rank);
+    if (route_rows16(T, k))
+        MOE_ROUTE16_LAUNCH(k_route_layout, grid, kThreads, (size_t)E * sizeof(uint32_t), logits,
+                           T, E, k, topk_idx, topk_w, ws.hist, ws.local_rank);
+    else
+        MOE_ROUTE_LAUNCH(k_route_layout_wide, grid, kGroupThreads, (size_t)E * sizeof(uint32_t),
+                         logits, T, E, k, topk_idx, topk_w, ws.hist, ws.local_rank);
 }
 
 void launch_hist(const int32_t* topk_idx, int64_t R, int32_t E, const Workspace& ws,
@@ -1712,18 +1921,36 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)T * k;
-    if (T > 0 && T <= kSmallTokens && R <= kSmallItems) {
-        // small batch: routing and layout in one workgroup, then the token-order packing
-        MOE_ROUTE_LAUNCH(k_route_layout_small, dim3(1), kGroupThreads, 0, logits, T, E, k,
-                         topk_idx, topk_w, out->token_row, out->row_token,
-                         count_outputs(out, n_ranks));
+    if (T > 0 && T <= kSmallTokens && k <= 16 && R <= kSmallItems && E <= 512) {
+        // small batch: routing and layout in one workgroup, then the token-order packing (up to
+        // 32 keys a lane: wider rows would not fit the registers next to the prefetched logits)
+        const CountOutputs co = count_outputs(out, n_ranks);
+        const int p16 = (int)ceil_div(E, 16);
+#define MOE_SMALL(PP)                                                                             \
+    k_route_layout_small<PP><<<1, kGroupThreads, 0, stream>>>(logits, T, E, k, topk_idx, topk_w,  \
+                                                              out->token_row, out->row_token, co)
+        if (p16 <= 1)
+            MOE_SMALL(1);
+        else if (p16 <= 2)
+            MOE_SMALL(2);
+        else if (p16 <= 4)
+            MOE_SMALL(4);
+        else if (p16 <= 8)
+            MOE_SMALL(8);
+        else if (p16 <= 16)
+            MOE_SMALL(16);
+        else if (p16 <= 24)
+            MOE_SMALL(24);
+        else
+            MOE_SMALL(32);
+#undef MOE_SMALL
         launch_pack(x, x_dtype, T, H, k, out->token_row, nullptr, nullptr, payload_dtype,
                     out->recv, out->recv_scales, R, stream);
         return launch_status();
     }
     const Workspace ws = carve_workspace(workspace, T, E, k);
     LayoutPlan plan;
-    if (T > 0 && fused_route_fits(T)) {
+    if (T > 0 && fused_route_fits(T, k)) {
         plan = route_plan(T, k);
         launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan, stream);
     } else {

@@ -78,7 +78,7 @@ def test_workspace_bytes():
     # 256 caller-given ids), the E expert totals, one u32 rank and one (row, token) pair per row,
     # in 256-byte aligned pieces
     R = 4096 * 8
-    nblk = 4096 // 16
+    nblk = max(4096 // 16, R // 256)
     lo = R * 4 + R * 8 + 2 * nblk * 384 * 4 + 384 * 4
     assert lo <= ws(4096, 384, 8) <= lo + 8 + 1280
     assert ws(4096, 384, 8) % 256 == 0

@@ -8,15 +8,14 @@
 //
 // The path moves bytes; it has no dense contraction, so it uses no MFMA. Every kernel is bound by
 // HBM bandwidth or by latency:
-//   k_route_topk     one wavefront per token: the lane-sorted candidates give up their heads over
-//                    k rounds of a wave-wide max (DPP row operations and four readlanes);
+//   k_route_topk     top-k routing, 16 lanes a token (k <= 16, large batches: k rounds of a row
+//                    maximum and a row minimum by DPP) or, as k_route_topk_wide, a wavefront a
+//                    token (lane-sorted candidates give up their heads over k wave-wide maxima);
 //   k_route_layout   the same routing, 16 tokens per workgroup, and in the same launch the
 //                    workgroup's expert histogram and the stable in-workgroup rank of every
 //                    (token, slot) from one LDS bit mask per expert;
 //   k_layout_hist    for caller-given expert ids: per block of items, stable in-block ranks from
 //                    per-wavefront LDS bit masks, and the block's expert histogram;
-//   k_route_layout_small  for small batches: routing, counting, offsets and row maps in one
-//                    workgroup, entirely in LDS;
 //   k_expert_scan    one wavefront per expert scans its blocks' counts into per-block prefixes
 //                    and the expert's total (many workgroups);
 //   k_layout_rows    every workgroup scans the expert totals into offsets in LDS, then writes
@@ -25,6 +24,9 @@
 //                    x (from the XCD's L2 after the first of the token's wavefronts) and a
 //                    16-byte non-temporal store per lane; the pieces of a row run side by side;
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
+//   k_decode_pack    batches of up to 512 routed tokens: every workgroup rebuilds the whole layout
+//                    in LDS from the ids (token bit masks, one block scan) and packs its pieces,
+//                    so layout and packing take one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
 //                    fp32 fused multiply-adds, one 16-byte store per 8 outputs;
 //   k_ep_recv_plan   expert-parallel receive: one workgroup turns a rank's per-(source, expert)
@@ -47,14 +49,15 @@ constexpr int kGroupThreads = 1024;      // 16-wavefront workgroups (route-layou
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kRouteTokens = kGroupWaves;   // route-layout workgroup, k > 16: a token a wave
 constexpr int kRouteTokens16 = kThreads / 16;   // route-layout workgroup, k <= 16: 16 lanes each
-constexpr int kSmallRound = kGroupThreads / 16; // tokens routed at once by the one-workgroup path
 constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
-constexpr int kSmallTokens = 64;         // small batches: routing and layout in one workgroup
-constexpr int kSmallItems = 2048;        //   (T <= 64 tokens, k <= 16, T*k <= 2048)
 constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
 constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
 constexpr int kCombineWaves = 2;         // wavefronts per combine workgroup
-constexpr int kXcds = 8;                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
+constexpr int kXcds = 8;
+constexpr int kDecodeTokens = 512;       // layout folded into packing: at most this many tokens
+constexpr int kDecodeThreads = 512;      //   (8 wavefronts a workgroup, two experts a thread)
+constexpr int kDecodeWaves = kDecodeThreads / 64;
+constexpr int kDecodeMaxGroups = 1024;   //   (grid-stride beyond this many workgroups)                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -757,103 +760,6 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
         rp.list[i] = make_int2(-1, -1);
 }
 
-// Routing and the whole layout of a small batch (T <= kSmallTokens, k <= 16, T*k <= kSmallItems)
-// in one workgroup, with no step between workgroups. Tokens are routed 64 at a time, 16 lanes a
-// token (the next round's logits are loaded before the current round is routed; one round is the
-// whole batch at the current limit, and routing is bound by this one CU's issue rate); the ids
-// stay in LDS and LDS counters count the experts. One block scan gives the expert offsets and the
-// count outputs. Then the tokens are taken 64 at a time, in order: token 64c + q sets bit q in the
-// LDS masks of its experts, and item (t, j) with expert e takes row
-// eoff[e] + run[e] + popcount(mask[e] & bits below q); run[e] then advances by popcount(mask[e]).
-// Routed ids are distinct within a token, so this is the stable (expert, token, slot) order.
-// LDS: ids [kSmallItems] u16, count/run [E] u32, offsets [E + 1] u32, masks [E] u64.
-template <int P>
-__global__ __launch_bounds__(kGroupThreads) void k_route_layout_small(
-    const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ token_row,
-    int32_t* __restrict__ row_token, CountOutputs co)
-{
-    __shared__ uint16_t ids[kSmallItems];
-    __shared__ uint32_t run[MOE_MAX_EXPERTS];
-    __shared__ uint32_t eoff[MOE_MAX_EXPERTS + 1];
-    __shared__ uint64_t mask[MOE_MAX_EXPERTS];
-    __shared__ uint32_t wave_tot[kGroupWaves];
-    const int tid = threadIdx.x, l16 = tid & 15;
-    const int q = tid >> 4;                              // token of the round, 0..63
-    for (int e = tid; e < E; e += kGroupThreads) {
-        run[e] = 0u;
-        mask[e] = 0ull;
-    }
-    __syncthreads();
-    float cur[P], nxt[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-        nxt[p] = 0.0f;
-    load_logits16<P>(logits + (int64_t)(q < T ? q : 0) * E, q < T ? E : 0, cur);
-    for (int c0 = 0; c0 < T; c0 += kSmallRound) {   // uniform across the workgroup
-        const int t = c0 + q;
-        const int tn = t + kSmallRound;
-        if (tn < T)
-            load_logits16<P>(logits + (int64_t)tn * E, E, nxt);
-        const int id = route_row16<P>(cur, E, k, t < T, topk_idx + (int64_t)t * k,
-                                      topk_w + (int64_t)t * k);
-        if (id >= 0) {
-            ids[t * k + l16] = (uint16_t)id;
-            atomicAdd(&run[id], 1u);
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-            cur[p] = nxt[p];
-    }
-    __syncthreads();
-    const uint32_t mine = tid < E ? run[tid] : 0u;    // E <= 1024: one expert per thread
-    uint32_t total = 0u;
-    const uint32_t ex = block_exclusive_scan<kGroupThreads>(mine, wave_tot, &total);
-    if (tid < E) {
-        eoff[tid] = ex;
-        run[tid] = 0u;
-    }
-    if (tid == 0)
-        eoff[E] = total;
-    __syncthreads();
-    const int epr = E / co.N;
-    if (tid < E) {
-        co.expert_offsets[tid] = (int32_t)eoff[tid];
-        co.expert_counts[tid] = (int32_t)(eoff[tid + 1] - eoff[tid]);
-    }
-    for (int r = tid; r < co.N; r += kGroupThreads) {
-        co.rank_offsets[r] = (int32_t)eoff[r * epr];
-        co.rank_counts[r] = (int32_t)(eoff[(r + 1) * epr] - eoff[r * epr]);
-    }
-    if (tid == 0) {
-        co.expert_offsets[E] = (int32_t)total;
-        co.rank_offsets[co.N] = (int32_t)total;
-    }
-    for (int c0 = 0; c0 < T; c0 += kSmallRound) {   // uniform across the workgroup
-        const int t = c0 + q;
-        const bool mine_item = t < T && l16 < k;
-        const int e = mine_item ? (int)ids[t * k + l16] : 0;
-        if (mine_item)
-            atomicOr((unsigned long long*)&mask[e], 1ull << q);
-        __syncthreads();
-        if (mine_item) {
-            const uint32_t row =
-                eoff[e] + run[e] + (uint32_t)__popcll(mask[e] & ((1ull << q) - 1ull));
-            token_row[t * k + l16] = (int32_t)row;
-            row_token[row] = t;
-        }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kGroupThreads) {
-            const uint64_t m = mask[ee];
-            if (m != 0ull) {
-                run[ee] += (uint32_t)__popcll(m);
-                mask[ee] = 0ull;
-            }
-        }
-        __syncthreads();
-    }
-}
-
 // ---------------------------------------------------------------------- expert-parallel receive --
 // Receiver half of dispatch for one rank, planning step. The S*L segments
 // (local expert l, source s) are taken in (l, s) order: segment (l, s) holds the
@@ -1100,6 +1006,27 @@ struct Load8<uint16_t> {
     }
 };
 
+// Block-scaled e4m3 of the 8 elements a lane holds, the 16 lanes of each DPP row forming one
+// 128-element block (every lane of the wavefront takes part in the row maximum): scale
+// s = amax / 448 (1 for an all-zero block, the division correctly rounded), codes e4m3(v / s),
+// packed little-endian into 8 bytes. Returns s.
+__device__ __forceinline__ float quantise8_e4m3(const float (&v)[8], u32x2& packed)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        amax = fmaxf(amax, fabsf(v[i]));
+    amax = max_row16_f32(amax);
+    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        q[i] = f32_to_e4m3(v[i] / s);
+    packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+    packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+    return s;
+}
+
 // fp8 packing, one wavefront per (token t, piece of 64 chunks of 8 elements), placed like the
 // token-order packing (tokens x, x+8, ... on XCD x). The 16 lanes of a DPP row hold the 128
 // elements of one scale block (H % 128 == 0, so a row of lanes is all active or all inactive);
@@ -1127,19 +1054,8 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
             v[i] = 0.0f;
     }
     const int32_t my_row = lane < pp.k ? pp.token_row[xi.token * pp.k + lane] : -1;
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        amax = fmaxf(amax, fabsf(v[i]));
-    amax = max_row16_f32(amax);
-    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;   // correctly rounded division
-    uint32_t q[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        q[i] = f32_to_e4m3(v[i] / s);
     u32x2 packed;
-    packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-    packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+    const float s = quantise8_e4m3(v, packed);
     for (int j = 0; j < pp.k; ++j) {
         const int32_t row = __builtin_amdgcn_readlane(my_row, j);
         if (row < 0 || (int64_t)row >= pp.row_limit)
@@ -1149,6 +1065,177 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
                                         reinterpret_cast<u32x2*>(recv + (int64_t)row * H) + c);
             if ((lane & 15) == 0)
                 recv_scales[(int64_t)row * (H / 128) + c / 16] = s;
+        }
+    }
+}
+
+// ------------------------------------------------------------- layout and packing in one launch --
+// Layout and packing of a routed batch of at most kDecodeTokens tokens in one launch: at decode
+// sizes every launch costs more than its work, so the scan and row kernels are folded into the
+// packing. Every workgroup rebuilds the whole layout in LDS from the routed ids (T*k of them, read
+// from L2): token t sets bit t % 32 of word t / 32 of the mask of each of its experts (a token's
+// routed experts are distinct); the popcount of an expert's mask is its count; one block scan
+// turns the counts into expert offsets; and item (t, j) with expert e takes row
+//   eoff[e] + (bits of e's mask below bit t),
+// the stable (expert, token, slot) order of the layout kernels. Wavefront m of the grid takes the
+// units (token, piece) m, m + waves, ...: lanes j < k compute the token's k rows, the wavefront of
+// piece 0 writes token_row and row_token, and every wavefront stores its piece of x to the k rows.
+// DECODE_COPY copies 16-byte chunks; the fp8 modes quantise 8 elements a lane (bf16 or fp32 x)
+// once, as the fp8 packing kernel does, and store codes and scales to the k rows. x and the ids of
+// the wavefront's first unit are loaded before the layout is built, so those loads overlap it.
+// Workgroup 0 writes the count outputs. LDS: masks [words][E] u32 (word-major), offsets [E+1] u32.
+enum DecodeMode { DECODE_COPY = 0, DECODE_FP8_BF16 = 1, DECODE_FP8_F32 = 2 };
+
+struct DecodePlan {
+    const void* x;
+    const int32_t* topk_idx;
+    int32_t* token_row;
+    int32_t* row_token;
+    void* recv;
+    float* recv_scales;
+    int32_t T, k, E, H;
+    int32_t words;        // ceil(T / 32) mask words per expert
+    int32_t chunks;       // lane chunks per row: 16 bytes (copy) or 8 elements (fp8)
+    int32_t pieces;       // ceil(chunks / 64)
+};
+
+template <int MODE>
+__global__ __launch_bounds__(kDecodeThreads) void k_decode_pack(DecodePlan dp, CountOutputs co)
+{
+    extern __shared__ uint32_t lds_dec[];
+    __shared__ uint32_t wave_tot[kDecodeWaves];
+    const int32_t E = dp.E, W = dp.words, k = dp.k;
+    uint32_t* mask = lds_dec;                            // [W][E]
+    uint32_t* eoff = lds_dec + (int64_t)W * E;           // [E + 1]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t waves = (int64_t)gridDim.x * kDecodeWaves;
+    const int64_t units = (int64_t)dp.T * dp.pieces;
+    int64_t u = (int64_t)blockIdx.x * kDecodeWaves + (tid >> 6);     // uniform per wavefront
+
+    // the first unit's payload and ids, in flight while the layout is built
+    u32x4 xv = {0u, 0u, 0u, 0u};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = 0.0f;
+    int32_t id = -1;
+    int64_t t = u / dp.pieces;
+    int c = (int)(u - t * dp.pieces) * 64 + lane;
+    if (u < units) {
+        if (c < dp.chunks) {
+            if constexpr (MODE == DECODE_COPY)
+                xv = static_cast<const u32x4*>(dp.x)[t * dp.chunks + c];
+            else if constexpr (MODE == DECODE_FP8_BF16)
+                Load8<uint16_t>::run(static_cast<const uint16_t*>(dp.x) + t * dp.H + c * 8, v);
+            else
+                Load8<float>::run(static_cast<const float*>(dp.x) + t * dp.H + c * 8, v);
+        }
+        if (lane < k)
+            id = dp.topk_idx[t * k + lane];
+    }
+
+    // the layout, in every workgroup
+    for (int i = tid; i < W * E; i += kDecodeThreads)
+        mask[i] = 0u;
+    __syncthreads();
+    const int32_t R = dp.T * k;
+    for (int32_t i = tid; i < R; i += kDecodeThreads) {
+        const int32_t e = dp.topk_idx[i];
+        if ((uint32_t)e < (uint32_t)E) {
+            const int32_t tt = i / k;
+            atomicOr(&mask[(tt >> 5) * E + e], 1u << (tt & 31));
+        }
+    }
+    __syncthreads();
+    const int e0 = 2 * tid, e1 = 2 * tid + 1;            // E <= 2 * kDecodeThreads
+    uint32_t c0 = 0u, c1 = 0u;
+    for (int w = 0; w < W; ++w) {
+        if (e0 < E)
+            c0 += (uint32_t)__popc(mask[w * E + e0]);
+        if (e1 < E)
+            c1 += (uint32_t)__popc(mask[w * E + e1]);
+    }
+    uint32_t total = 0u;
+    const uint32_t ex = block_exclusive_scan<kDecodeThreads>(c0 + c1, wave_tot, &total);
+    if (e0 < E)
+        eoff[e0] = ex;
+    if (e1 < E)
+        eoff[e1] = ex + c0;
+    if (tid == 0)
+        eoff[E] = total;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        const int epr = E / co.N;
+        for (int e = tid; e < E; e += kDecodeThreads) {
+            co.expert_offsets[e] = (int32_t)eoff[e];
+            co.expert_counts[e] = (int32_t)(eoff[e + 1] - eoff[e]);
+        }
+        for (int r = tid; r < co.N; r += kDecodeThreads) {
+            co.rank_offsets[r] = (int32_t)eoff[r * epr];
+            co.rank_counts[r] = (int32_t)(eoff[(r + 1) * epr] - eoff[r * epr]);
+        }
+        if (tid == 0) {
+            co.expert_offsets[E] = (int32_t)total;
+            co.rank_offsets[co.N] = (int32_t)total;
+        }
+    }
+
+    // the wavefront's units; no barrier from here on
+    for (bool first = true; u < units; u += waves, first = false) {
+        if (!first) {
+            t = u / dp.pieces;
+            c = (int)(u - t * dp.pieces) * 64 + lane;
+            if (c < dp.chunks) {
+                if constexpr (MODE == DECODE_COPY)
+                    xv = static_cast<const u32x4*>(dp.x)[t * dp.chunks + c];
+                else if constexpr (MODE == DECODE_FP8_BF16)
+                    Load8<uint16_t>::run(static_cast<const uint16_t*>(dp.x) + t * dp.H + c * 8,
+                                         v);
+                else
+                    Load8<float>::run(static_cast<const float*>(dp.x) + t * dp.H + c * 8, v);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    v[i] = 0.0f;
+            }
+            id = lane < k ? dp.topk_idx[t * k + lane] : -1;
+        }
+        int32_t row = -1;
+        if ((uint32_t)id < (uint32_t)E) {
+            // the token's own bit is set in the mask, so row < eoff[id + 1] <= R
+            const int tw = (int)(t >> 5);
+            uint32_t r = eoff[id];
+            for (int w = 0; w < tw; ++w)
+                r += (uint32_t)__popc(mask[w * E + id]);
+            r += (uint32_t)__popc(mask[tw * E + id] & ((1u << (t & 31)) - 1u));
+            row = (int32_t)r;
+        }
+        if (c < 64 && lane < k) {                        // piece 0: the row maps
+            dp.token_row[t * k + lane] = row;
+            if (row >= 0)
+                dp.row_token[row] = (int32_t)t;
+        }
+        const bool active = c < dp.chunks;
+        if constexpr (MODE == DECODE_COPY) {
+            u32x4* rv = static_cast<u32x4*>(dp.recv);
+            for (int j = 0; j < k; ++j) {
+                const int32_t rj = __builtin_amdgcn_readlane(row, j);
+                if (rj >= 0 && active)
+                    __builtin_nontemporal_store(xv, rv + (int64_t)rj * dp.chunks + c);
+            }
+        } else {
+            u32x2 packed;
+            const float s = quantise8_e4m3(v, packed);
+            uint8_t* rv = static_cast<uint8_t*>(dp.recv);
+            for (int j = 0; j < k; ++j) {
+                const int32_t rj = __builtin_amdgcn_readlane(row, j);
+                if (rj >= 0 && active) {
+                    __builtin_nontemporal_store(
+                        packed, reinterpret_cast<u32x2*>(rv + (int64_t)rj * dp.H) + c);
+                    if ((lane & 15) == 0)
+                        dp.recv_scales[(int64_t)rj * (dp.H / 128) + c / 16] = s;
+                }
+            }
         }
     }
 }
@@ -1777,6 +1864,48 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
                                                                pp, rv, recv_scales);
 }
 
+// Layout and packing of a routed batch in one launch (the ids must be the router's, distinct
+// within a token): up to kDecodeTokens tokens, with the masks and offsets in 64 KB of LDS.
+inline size_t decode_lds_bytes(int32_t T, int32_t E)
+{
+    return ((size_t)ceil_div(T, 32) * E + E + 1) * sizeof(uint32_t);
+}
+
+inline bool decode_fits(int32_t T, int32_t E)
+{
+    return T >= 1 && T <= kDecodeTokens && decode_lds_bytes(T, E) <= 64 * 1024;
+}
+
+void launch_decode_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t E,
+                        int32_t k, const int32_t* topk_idx, moe_dtype_t payload_dtype,
+                        const moe_dispatch_out_t* out, const CountOutputs& co, hipStream_t stream)
+{
+    const bool fp8 = payload_dtype == MOE_FP8_E4M3;
+    DecodePlan dp;
+    dp.x = x;
+    dp.topk_idx = topk_idx;
+    dp.token_row = out->token_row;
+    dp.row_token = out->row_token;
+    dp.recv = out->recv;
+    dp.recv_scales = out->recv_scales;
+    dp.T = T;
+    dp.k = k;
+    dp.E = E;
+    dp.H = H;
+    dp.words = (int32_t)ceil_div(T, 32);
+    dp.chunks = fp8 ? H / 8 : (int32_t)((int64_t)H * (int64_t)dtype_size(x_dtype) / 16);
+    dp.pieces = (int32_t)ceil_div(dp.chunks, 64);
+    const int64_t groups = ceil_div((int64_t)T * dp.pieces, kDecodeWaves);
+    const dim3 grid((unsigned)(groups < kDecodeMaxGroups ? groups : kDecodeMaxGroups));
+    const size_t lds = decode_lds_bytes(T, E);
+    if (!fp8)
+        k_decode_pack<DECODE_COPY><<<grid, kDecodeThreads, lds, stream>>>(dp, co);
+    else if (x_dtype == MOE_F32)
+        k_decode_pack<DECODE_FP8_F32><<<grid, kDecodeThreads, lds, stream>>>(dp, co);
+    else
+        k_decode_pack<DECODE_FP8_BF16><<<grid, kDecodeThreads, lds, stream>>>(dp, co);
+}
+
 template <typename YT, typename OT>
 void launch_combine_typed(const void* y, int32_t T, int32_t H, int32_t k,
                           const int32_t* token_row, const float* topk_w, void* out, int32_t R,
@@ -1921,31 +2050,11 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)T * k;
-    if (T > 0 && T <= kSmallTokens && k <= 16 && R <= kSmallItems && E <= 512) {
-        // small batch: routing and layout in one workgroup, then the token-order packing (up to
-        // 32 keys a lane: wider rows would not fit the registers next to the prefetched logits)
-        const CountOutputs co = count_outputs(out, n_ranks);
-        const int p16 = (int)ceil_div(E, 16);
-#define MOE_SMALL(PP)                                                                             \
-    k_route_layout_small<PP><<<1, kGroupThreads, 0, stream>>>(logits, T, E, k, topk_idx, topk_w,  \
-                                                              out->token_row, out->row_token, co)
-        if (p16 <= 1)
-            MOE_SMALL(1);
-        else if (p16 <= 2)
-            MOE_SMALL(2);
-        else if (p16 <= 4)
-            MOE_SMALL(4);
-        else if (p16 <= 8)
-            MOE_SMALL(8);
-        else if (p16 <= 16)
-            MOE_SMALL(16);
-        else if (p16 <= 24)
-            MOE_SMALL(24);
-        else
-            MOE_SMALL(32);
-#undef MOE_SMALL
-        launch_pack(x, x_dtype, T, H, k, out->token_row, nullptr, nullptr, payload_dtype,
-                    out->recv, out->recv_scales, R, stream);
+    if (decode_fits(T, E)) {
+        // decode sizes: routing, then layout and packing in one launch
+        launch_route(logits, T, E, k, topk_idx, topk_w, stream);
+        launch_decode_pack(x, x_dtype, T, H, E, k, topk_idx, payload_dtype, out,
+                           count_outputs(out, n_ranks), stream);
         return launch_status();
     }
     const Workspace ws = carve_workspace(workspace, T, E, k);

@@ -158,9 +158,19 @@ EDGE = [
     (4500, 512, 256, 8, 16, "bf16", "bf16"),    # T*k = 36000: several rows per layout block
     (9000, 256, 1024, 8, 64, "bf16", "bf16"),   # E at its maximum; T*k = 72000 > 64 * 1024
     (3, 128, 1024, 64, 1024, "bf16", "fp8_e4m3"),   # k at its maximum, N = E = 1024
-    (32, 512, 256, 8, 32, "bf16", "fp8_e4m3"),  # most tokens the one-workgroup routing takes
+    (32, 512, 256, 8, 32, "bf16", "fp8_e4m3"),  # one mask word a token block
     (16384, 128, 64, 2, 4, "bf16", "bf16"),     # most tokens the fused route-layout takes
     (16401, 128, 64, 2, 4, "f32", "f32"),       # one token more: separate route + histogram
+    # layout folded into packing (up to 512 tokens through moe_route_dispatch)
+    (100, 4104, 64, 4, 8, "bf16", "bf16"),      # ragged 16-byte tail, tokens across 4 mask words
+    (200, 256, 384, 32, 48, "f32", "f32"),      # k > 16 (a wavefront a token in routing)
+    (129, 512, 8, 8, 2, "bf16", "bf16"),        # k = E: every token on every expert
+    (256, 7168, 1024, 8, 64, "bf16", "fp8_e4m3"),   # E at its maximum, fp8
+    (256, 1024, 1024, 64, 8, "f32", "fp8_e4m3"),    # k at its maximum, fp8 from fp32
+    (448, 512, 1024, 2, 4, "bf16", "bf16"),     # most tokens that fit 64 KB of masks at E = 1024
+    (449, 512, 1024, 2, 4, "bf16", "bf16"),     # one token more: the multi-launch layout
+    (512, 1536, 256, 8, 32, "bf16", "bf16"),    # most tokens the one-launch layout takes
+    (513, 512, 64, 2, 4, "bf16", "bf16"),       # one token more: the multi-launch layout
 ]
 
 
@@ -201,10 +211,11 @@ def test_edge_shapes(T, H, E, k, N, x_dtype, payload):
     _check_payload(buf, d, payload)
 
 
-def test_all_tokens_on_one_expert_and_ties():
+@pytest.mark.parametrize("T", [2000, 200])
+def test_all_tokens_on_one_expert_and_ties(T):
     """Every token picks expert 5 first (hot spot); the rest of each row ties at 0."""
-    T, H, E, k, N = 2000, 256, 32, 4, 8
-    _announce("edge hot expert + ties")
+    H, E, k, N = 256, 32, 4, 8
+    _announce(f"edge hot expert + ties T={T}")
     logits = np.zeros((T, E), np.float32)
     logits[:, 5] = 3.0
     logits[::3, 7] = -0.0

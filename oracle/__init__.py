@@ -59,6 +59,7 @@ def _load():
             "oracle_ep_partial_rows": [P, I, I, I, I, I, I, I, P, P],
             "oracle_ep_reduce": [P, I, I, I, I, I, I, I, P, I, I, P, P, P, P, P],
             "oracle_ep_combine_reduced": [P, I, I, I, I, P, P, I],
+            "oracle_check_topk": [P, I, I, I, P],
         }.items():
             fn = getattr(lib, name)
             fn.argtypes = args
@@ -279,3 +280,12 @@ def ep_combine_reduced(partials, dtype: str, part_row, out_dtype: str) -> np.nda
     if rc:
         raise ValueError(f"oracle_ep_combine_reduced rejected its arguments (code {rc})")
     return out
+
+
+def check_topk(topk_idx, E: int) -> tuple:
+    """(ids outside [0, E), in-range ids repeating an earlier slot of their token)."""
+    idx = _c(topk_idx, np.int32)
+    T, k = idx.shape
+    counts = np.zeros(2, np.int64)
+    assert _load().oracle_check_topk(_p(idx), T, k, E, _p(counts)) == 0
+    return int(counts[0]), int(counts[1])

@@ -636,3 +636,33 @@ int oracle_ep_combine_reduced(const void* partials, int32_t dtype, int32_t T, in
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * The routing precondition of dispatch. Dispatch is handed, for every token, the experts it goes
+ * to ("MoE all-to-all over EFA"); the router picks k of the E experts for each token
+ * ("Introductie"), so every id names an expert and no token names one expert twice.
+ * counts[0] = number of slots (t, j) whose id lies outside [0, E);
+ * counts[1] = number of slots (t, j) whose id lies in [0, E) and equals the id of an earlier slot
+ *             j' < j of the same token (a token naming one expert three times counts 2).
+ * ---------------------------------------------------------------------------------------------- */
+int oracle_check_topk(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int64_t* counts)
+{
+    if (T < 0 || k < 1 || E < 1)
+        return 1;
+    counts[0] = 0;
+    counts[1] = 0;
+    for (int64_t t = 0; t < T; t++)
+        for (int32_t j = 0; j < k; j++) {
+            const int32_t id = topk_idx[t * k + j];
+            if (id < 0 || id >= E) {
+                counts[0]++;
+                continue;
+            }
+            for (int32_t jj = 0; jj < j; jj++)
+                if (topk_idx[t * k + jj] == id) {
+                    counts[1]++;
+                    break;
+                }
+        }
+    return 0;
+}

@@ -16,6 +16,13 @@ from conftest import ROOT
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 
 MUTANTS = {
+    "check_last_expert_out_of_range": ("if (id < 0 || id >= E) {\n                counts[0]++;",
+                                       "if (id < 0 || id > E) {\n                counts[0]++;",
+                                       "test_oracle_check.py"),
+    "check_repeats_counted_per_pair": ("counts[1]++;\n                    break;",
+                                       "counts[1]++;", "test_oracle_check.py"),
+    "check_drops_token_offset": ("if (topk_idx[t * k + jj] == id) {", "if (topk_idx[jj] == id) {",
+                                 "test_oracle_check.py"),
     "tie_to_higher_id": ("(l[a] == l[b] && a < b)", "(l[a] == l[b] && a > b)",
                          "test_oracle_route.py"),
     "no_renormalisation": ("(float)(p[idx[j]] / kept)", "(float)(p[idx[j]])",

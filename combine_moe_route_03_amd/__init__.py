@@ -10,7 +10,7 @@ _EXPORTS = ("moe_route_topk", "moe_dispatch_workspace_bytes", "moe_dispatch_layo
             "moe_status_str", "alloc_dispatch_out", "alloc_workspace", "DispatchBuffers",
             "MoeError", "moe_ep_capacity", "moe_ep_send", "moe_ep_recv", "moe_ep_return",
             "moe_ep_combine", "moe_ep_partial_rows", "moe_ep_reduce", "moe_ep_reduce_workspace",
-            "moe_ep_combine_reduced")
+            "moe_ep_combine_reduced", "moe_check_topk")
 
 
 def __getattr__(name):

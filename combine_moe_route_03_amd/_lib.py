@@ -68,10 +68,11 @@ def load() -> ctypes.CDLL:
         lib.moe_ep_reduce_workspace_bytes.restype = Z
         lib.moe_ep_reduce.argtypes = [P, I, I, I, I, I, I, I, P, I, I, P, P, P, P, I, P, P, Z, P]
         lib.moe_ep_combine_reduced.argtypes = [P, I, I, I, I, P, I, P, I, P]
+        lib.moe_check_topk.argtypes = [P, I, I, I, P, P]
         for fn in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_dispatch",
                    "moe_route_dispatch", "moe_combine", "moe_ep_send", "moe_ep_recv",
                    "moe_ep_return", "moe_ep_combine", "moe_ep_partial_rows", "moe_ep_reduce",
-                   "moe_ep_combine_reduced"):
+                   "moe_ep_combine_reduced", "moe_check_topk"):
             getattr(lib, fn).restype = I
         _lib = lib
     return _lib
@@ -120,6 +121,31 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: Optional[torch.Tensor
     return topk_idx, topk_w
 
 
+def moe_check_topk(topk_idx: torch.Tensor, E: int, counts: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Device int32 [2]: slots with an id outside [0, E), in-range slots repeating an earlier slot
+    of their token. Enqueued on the stream; read it after the stream has finished."""
+    T, k = topk_idx.shape
+    if counts is None:
+        counts = torch.empty(2, dtype=torch.int32, device=topk_idx.device)
+    assert topk_idx.dtype == torch.int32 and topk_idx.is_contiguous()
+    _check("moe_check_topk", load().moe_check_topk(_ptr(topk_idx), T, k, E, _ptr(counts),
+                                                   _stream(stream)))
+    return counts
+
+
+def _debug_check_ids(fn: str, topk_idx: torch.Tensor, E: int, stream) -> None:
+    """With MOE_ROUTE_DEBUG=1, check caller-given ids on the GPU before they are dispatched and
+    raise ValueError naming what is wrong (this waits for the stream)."""
+    if os.environ.get("MOE_ROUTE_DEBUG", "0") != "1":
+        return
+    counts = moe_check_topk(topk_idx, E, stream=stream)
+    bad, rep = (int(v) for v in counts.cpu().tolist())
+    if bad or rep:
+        raise ValueError(f"{fn}: {bad} expert ids outside [0, {E}) and {rep} repeated within a "
+                         f"token (MOE_ROUTE_DEBUG=1)")
+
+
 def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
     return int(load().moe_dispatch_workspace_bytes(T, E, k))
 
@@ -166,6 +192,7 @@ def alloc_workspace(T: int, E: int, k: int, device="cuda") -> torch.Tensor:
 def moe_dispatch_layout(topk_idx: torch.Tensor, E: int, n_ranks: int, out: DispatchBuffers,
                         workspace: torch.Tensor, stream=None) -> DispatchBuffers:
     T, k = topk_idx.shape
+    _debug_check_ids("moe_dispatch_layout", topk_idx, E, stream)
     st = out.as_struct()
     _check("moe_dispatch_layout", load().moe_dispatch_layout(
         _ptr(topk_idx), T, k, E, n_ranks, ctypes.byref(st), _ptr(workspace),
@@ -187,6 +214,7 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, n_ranks: int,
                  out: DispatchBuffers, workspace: torch.Tensor, stream=None) -> DispatchBuffers:
     T, H = x.shape
     k = topk_idx.shape[1]
+    _debug_check_ids("moe_dispatch", topk_idx, E, stream)
     st = out.as_struct()
     _check("moe_dispatch", load().moe_dispatch(
         _ptr(x), _dtype_code(x), T, H, _ptr(topk_idx), k, E, n_ranks,
@@ -238,6 +266,7 @@ def moe_ep_send(x: torch.Tensor, topk_idx: torch.Tensor, E: int, n_ranks: int, s
     """Sender half of dispatch for one source; fills its regions, counts and send_row."""
     T, H = x.shape
     k = topk_idx.shape[1]
+    _debug_check_ids("moe_ep_send", topk_idx, E, stream)
     _check("moe_ep_send", load().moe_ep_send(
         _ptr(x), _dtype_code(x), T, H, _ptr(topk_idx), k, E, n_ranks, source, n_sources, cap,
         _ptr(regions), _ptr(region_counts), _ptr(send_row), _ptr(workspace),

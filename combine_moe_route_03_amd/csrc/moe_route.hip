@@ -760,6 +760,44 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
         rp.list[i] = make_int2(-1, -1);
 }
 
+// ------------------------------------------------------------ routing precondition check --
+// What dispatch takes for granted about ids that do not come from the router: every slot names one
+// of the E experts, and no token names one expert twice. counts[0] += slots whose id lies outside
+// [0, E); counts[1] += slots whose in-range id equals the id of an earlier slot of the same token.
+// Grid-stride over the slots; each wavefront adds its two sums with one atomic each to the counts
+// that k_zero_i32 cleared before it.
+__global__ __launch_bounds__(64) void k_zero_i32(int32_t* __restrict__ p, int32_t n)
+{
+    if ((int32_t)threadIdx.x < n)
+        p[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void k_check_topk(const int32_t* __restrict__ topk_idx,
+                                                         int64_t R, int32_t k, int32_t E,
+                                                         int32_t* __restrict__ counts)
+{
+    uint32_t bad = 0u, rep = 0u;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < R; i += stride) {
+        const int32_t id = topk_idx[i];
+        if ((uint32_t)id >= (uint32_t)E) {
+            ++bad;
+            continue;
+        }
+        for (int64_t q = i - i % k; q < i; ++q)
+            if (topk_idx[q] == id) {
+                ++rep;
+                break;
+            }
+    }
+    bad = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan_u32(bad), 63);
+    rep = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan_u32(rep), 63);
+    if ((threadIdx.x & 63) == 0 && (bad | rep) != 0u) {
+        atomicAdd(&counts[0], (int32_t)bad);
+        atomicAdd(&counts[1], (int32_t)rep);
+    }
+}
+
 // ---------------------------------------------------------------------- expert-parallel receive --
 // Receiver half of dispatch for one rank, planning step. The S*L segments
 // (local expert l, source s) are taken in (l, s) order: segment (l, s) holds the
@@ -2073,6 +2111,23 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
                      count_outputs(out, n_ranks), nullptr, ws, plan, wp, stream);
     launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
                 out->recv_scales, R, stream);
+    return launch_status();
+}
+
+moe_status_t moe_check_topk(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                            int32_t* counts, hipStream_t stream)
+{
+    if (T < 0 || k < 1 || E < 1 || (int64_t)T * k > INT32_MAX || !counts)
+        return MOE_ERR_INVALID;
+    if (T > 0 && !topk_idx)
+        return MOE_ERR_INVALID;
+    k_zero_i32<<<1, 64, 0, stream>>>(counts, 2);
+    const int64_t R = (int64_t)T * k;
+    if (R > 0) {
+        const int64_t g = ceil_div(R, (int64_t)kThreads);
+        k_check_topk<<<(unsigned)(g < 1024 ? g : 1024), kThreads, 0, stream>>>(topk_idx, R, k, E,
+                                                                              counts);
+    }
     return launch_status();
 }
 

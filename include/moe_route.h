@@ -280,6 +280,22 @@ moe_status_t moe_ep_combine_reduced(const void* partials, moe_dtype_t dtype, int
                                     int32_t partial_rows, void* out, moe_dtype_t out_dtype,
                                     hipStream_t stream);
 
+/*
+ * moe_check_topk -- check of what dispatch takes for granted about the expert ids it is handed
+ * ("MoE all-to-all over EFA": dispatch receives every token with its experts; "Introductie": the
+ * router picks k of the E experts of each token). For ids that do not come from the router.
+ *   topk_idx [T, k] int32 (device), counts [2] int32 (device) out:
+ *   counts[0] = slots (t, j) whose id lies outside [0, E);
+ *   counts[1] = slots whose id lies in [0, E) and equals the id of an earlier slot of the same
+ *               token (a token naming one expert three times counts 2).
+ * The dispatch calls skip out-of-range ids (their token_row is -1) and order repeated ids by
+ * (expert, token, slot); this call tells a caller that either happened. Enqueued on `stream`
+ * like every other call: read counts after the stream has finished. Requires k >= 1, E >= 1,
+ * T * k <= INT32_MAX (else MOE_ERR_INVALID). T = 0 writes two zeros.
+ */
+moe_status_t moe_check_topk(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                            int32_t* counts, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_str(moe_status_t status);
 

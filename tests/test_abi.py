@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_function():
                             "moe_ep_capacity", "moe_ep_send", "moe_ep_recv", "moe_ep_return",
                             "moe_ep_combine", "moe_ep_partial_rows",
                             "moe_ep_reduce_workspace_bytes", "moe_ep_reduce",
-                            "moe_ep_combine_reduced"])
+                            "moe_ep_combine_reduced", "moe_check_topk"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -266,6 +266,17 @@ def test_combine_validation():
     assert f(A16, BF16, 4, 256, 2, A16, None, A16b, BF16, S0) == moe.MOE_ERR_INVALID
     assert f(A16, BF16, 4, 256, 0, A16, A16, A16b, BF16, S0) == moe.MOE_ERR_INVALID
     assert f(None, BF16, 0, 256, 2, None, None, None, BF16, S0) == moe.MOE_OK
+
+
+def test_check_topk_validation():
+    f = moe.load().moe_check_topk
+    I = moe.MOE_ERR_INVALID
+    assert f(A16, 4, 0, 8, A16b, S0) == I           # k < 1
+    assert f(A16, 4, 2, 0, A16b, S0) == I           # E < 1
+    assert f(A16, -1, 2, 8, A16b, S0) == I          # T < 0
+    assert f(A16, 4, 2, 8, None, S0) == I           # no counts
+    assert f(None, 4, 2, 8, A16b, S0) == I          # no ids
+    assert f(A16, 2**30, 4, 8, A16b, S0) == I       # T * k > INT32_MAX
 
 
 def test_product_path_does_not_reference_the_oracle():

@@ -24,9 +24,9 @@
 //                    x (from the XCD's L2 after the first of the token's wavefronts) and a
 //                    16-byte non-temporal store per lane; the pieces of a row run side by side;
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
-//   k_decode_pack    batches of up to 512 routed tokens: every workgroup rebuilds the whole layout
-//                    in LDS from the ids (token bit masks, one block scan) and packs its pieces,
-//                    so layout and packing take one launch;
+//   k_layout_pack    batches of up to 512 tokens: every workgroup rebuilds the whole layout in
+//                    LDS from the ids (LDS counts, one block scan, token bit masks for the ranks)
+//                    and packs its pieces, so layout and packing take one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
 //                    fp32 fused multiply-adds, one 16-byte store per 8 outputs;
 //   k_ep_recv_plan   expert-parallel receive: one workgroup turns a rank's per-(source, expert)
@@ -54,10 +54,10 @@ constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
 constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
 constexpr int kCombineWaves = 2;         // wavefronts per combine workgroup
 constexpr int kXcds = 8;
-constexpr int kDecodeTokens = 512;       // layout folded into packing: at most this many tokens
-constexpr int kDecodeThreads = 512;      //   (8 wavefronts a workgroup, two experts a thread)
-constexpr int kDecodeWaves = kDecodeThreads / 64;
-constexpr int kDecodeMaxGroups = 1024;   //   (grid-stride beyond this many workgroups)                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
+constexpr int kLpTokens = 512;           // layout folded into packing: at most this many tokens
+constexpr int kLpThreads = 512;          //   (8 wavefronts a workgroup, two experts a thread)
+constexpr int kLpWaves = kLpThreads / 64;
+constexpr int kLpMaxGroups = 1024;       //   (grid-stride beyond this many workgroups)                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -1108,23 +1108,29 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
 }
 
 // ------------------------------------------------------------- layout and packing in one launch --
-// Layout and packing of a routed batch of at most kDecodeTokens tokens in one launch: at decode
-// sizes every launch costs more than its work, so the scan and row kernels are folded into the
-// packing. Every workgroup rebuilds the whole layout in LDS from the routed ids (T*k of them, read
-// from L2): token t sets bit t % 32 of word t / 32 of the mask of each of its experts (a token's
-// routed experts are distinct); the popcount of an expert's mask is its count; one block scan
-// turns the counts into expert offsets; and item (t, j) with expert e takes row
-//   eoff[e] + (bits of e's mask below bit t),
-// the stable (expert, token, slot) order of the layout kernels. Wavefront m of the grid takes the
-// units (token, piece) m, m + waves, ...: lanes j < k compute the token's k rows, the wavefront of
-// piece 0 writes token_row and row_token, and every wavefront stores its piece of x to the k rows.
-// DECODE_COPY copies 16-byte chunks; the fp8 modes quantise 8 elements a lane (bf16 or fp32 x)
-// once, as the fp8 packing kernel does, and store codes and scales to the k rows. x and the ids of
-// the wavefront's first unit are loaded before the layout is built, so those loads overlap it.
-// Workgroup 0 writes the count outputs. LDS: masks [words][E] u32 (word-major), offsets [E+1] u32.
-enum DecodeMode { DECODE_COPY = 0, DECODE_FP8_BF16 = 1, DECODE_FP8_F32 = 2 };
+// Layout and packing of a batch of at most kLpTokens tokens in one launch: at these sizes every
+// launch costs more than its work, so the scan and row kernels are folded into the packing. Every
+// workgroup rebuilds the whole layout in LDS from the T*k expert ids (read from L2):
+//   - counts: one LDS atomic add per slot (order does not matter for a count); one block scan turns
+//     them into expert offsets;
+//   - ranks: token t sets bit t % 32 of word t / 32 of the mask of each of its experts. When no
+//     token names an expert twice (always so for routed ids), item (t, j) with expert e takes row
+//       eoff[e] + (bits of e's mask below bit t),
+//     the stable (expert, token, slot) order of the layout kernels. A token naming an expert twice
+//     finds its bit already set when inserting it; then every workgroup (they all read the same
+//     ids) takes the exact rank instead: the wavefront counts the earlier slots with the same
+//     expert, 64 slots a step.
+// Wavefront m of the grid takes the units (token, piece) m, m + waves, ...: lanes j < k compute the
+// token's k rows, the wavefront of piece 0 writes token_row and row_token, and every wavefront
+// stores its piece of x to the k rows. LP_COPY copies 16-byte chunks; the fp8 modes quantise 8
+// elements a lane (bf16 or fp32 x) once, as the fp8 packing kernel does, and store codes and scales
+// to the k rows; LP_LAYOUT writes the row maps only (one unit a token). x and the ids of the
+// wavefront's first unit are loaded before the layout is built, so those loads overlap it.
+// Out-of-range ids are skipped (token_row -1). Workgroup 0 writes the count outputs.
+// LDS: masks [words][E] u32 (word-major), offsets [E + 1] u32.
+enum LayoutPackMode { LP_COPY = 0, LP_FP8_BF16 = 1, LP_FP8_F32 = 2, LP_LAYOUT = 3 };
 
-struct DecodePlan {
+struct LayoutPackPlan {
     const void* x;
     const int32_t* topk_idx;
     int32_t* token_row;
@@ -1133,22 +1139,35 @@ struct DecodePlan {
     float* recv_scales;
     int32_t T, k, E, H;
     int32_t words;        // ceil(T / 32) mask words per expert
-    int32_t chunks;       // lane chunks per row: 16 bytes (copy) or 8 elements (fp8)
-    int32_t pieces;       // ceil(chunks / 64)
+    int32_t chunks;       // lane chunks per row: 16 bytes (copy) or 8 elements (fp8); 0 for layout
+    int32_t pieces;       // ceil(chunks / 64), at least 1
 };
 
 template <int MODE>
-__global__ __launch_bounds__(kDecodeThreads) void k_decode_pack(DecodePlan dp, CountOutputs co)
+__device__ __forceinline__ void lp_load(const LayoutPackPlan& lp, int64_t t, int c, u32x4& xv,
+                                        float (&v)[8])
 {
-    extern __shared__ uint32_t lds_dec[];
-    __shared__ uint32_t wave_tot[kDecodeWaves];
-    const int32_t E = dp.E, W = dp.words, k = dp.k;
-    uint32_t* mask = lds_dec;                            // [W][E]
-    uint32_t* eoff = lds_dec + (int64_t)W * E;           // [E + 1]
+    if constexpr (MODE == LP_COPY)
+        xv = static_cast<const u32x4*>(lp.x)[t * lp.chunks + c];
+    else if constexpr (MODE == LP_FP8_BF16)
+        Load8<uint16_t>::run(static_cast<const uint16_t*>(lp.x) + t * lp.H + c * 8, v);
+    else if constexpr (MODE == LP_FP8_F32)
+        Load8<float>::run(static_cast<const float*>(lp.x) + t * lp.H + c * 8, v);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, CountOutputs co)
+{
+    extern __shared__ uint32_t lds_lp[];
+    __shared__ uint32_t wave_tot[kLpWaves];
+    __shared__ uint32_t repeated;
+    const int32_t E = lp.E, W = lp.words, k = lp.k;
+    uint32_t* mask = lds_lp;                             // [W][E]
+    uint32_t* eoff = lds_lp + (int64_t)W * E;            // [E + 1]: counts, then offsets
     const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t waves = (int64_t)gridDim.x * kDecodeWaves;
-    const int64_t units = (int64_t)dp.T * dp.pieces;
-    int64_t u = (int64_t)blockIdx.x * kDecodeWaves + (tid >> 6);     // uniform per wavefront
+    const int64_t waves = (int64_t)gridDim.x * kLpWaves;
+    const int64_t units = (int64_t)lp.T * lp.pieces;
+    int64_t u = (int64_t)blockIdx.x * kLpWaves + (tid >> 6);       // uniform per wavefront
 
     // the first unit's payload and ids, in flight while the layout is built
     u32x4 xv = {0u, 0u, 0u, 0u};
@@ -1157,44 +1176,40 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_pack(DecodePlan dp, C
     for (int i = 0; i < 8; ++i)
         v[i] = 0.0f;
     int32_t id = -1;
-    int64_t t = u / dp.pieces;
-    int c = (int)(u - t * dp.pieces) * 64 + lane;
+    int64_t t = u / lp.pieces;
+    int c = (int)(u - t * lp.pieces) * 64 + lane;
     if (u < units) {
-        if (c < dp.chunks) {
-            if constexpr (MODE == DECODE_COPY)
-                xv = static_cast<const u32x4*>(dp.x)[t * dp.chunks + c];
-            else if constexpr (MODE == DECODE_FP8_BF16)
-                Load8<uint16_t>::run(static_cast<const uint16_t*>(dp.x) + t * dp.H + c * 8, v);
-            else
-                Load8<float>::run(static_cast<const float*>(dp.x) + t * dp.H + c * 8, v);
-        }
+        if (c < lp.chunks)
+            lp_load<MODE>(lp, t, c, xv, v);
         if (lane < k)
-            id = dp.topk_idx[t * k + lane];
+            id = lp.topk_idx[t * k + lane];
     }
 
     // the layout, in every workgroup
-    for (int i = tid; i < W * E; i += kDecodeThreads)
+    for (int i = tid; i < W * E; i += kLpThreads)
         mask[i] = 0u;
+    for (int i = tid; i <= E; i += kLpThreads)
+        eoff[i] = 0u;
+    if (tid == 0)
+        repeated = 0u;
     __syncthreads();
-    const int32_t R = dp.T * k;
-    for (int32_t i = tid; i < R; i += kDecodeThreads) {
-        const int32_t e = dp.topk_idx[i];
+    const int32_t R = lp.T * k;
+    for (int32_t i = tid; i < R; i += kLpThreads) {
+        const int32_t e = lp.topk_idx[i];
         if ((uint32_t)e < (uint32_t)E) {
             const int32_t tt = i / k;
-            atomicOr(&mask[(tt >> 5) * E + e], 1u << (tt & 31));
+            const uint32_t bit = 1u << (tt & 31);
+            if (atomicOr(&mask[(tt >> 5) * E + e], bit) & bit)
+                repeated = 1u;                           // the token names e twice
+            atomicAdd(&eoff[e], 1u);
         }
     }
     __syncthreads();
-    const int e0 = 2 * tid, e1 = 2 * tid + 1;            // E <= 2 * kDecodeThreads
-    uint32_t c0 = 0u, c1 = 0u;
-    for (int w = 0; w < W; ++w) {
-        if (e0 < E)
-            c0 += (uint32_t)__popc(mask[w * E + e0]);
-        if (e1 < E)
-            c1 += (uint32_t)__popc(mask[w * E + e1]);
-    }
+    const int e0 = 2 * tid, e1 = 2 * tid + 1;            // E <= 2 * kLpThreads
+    const uint32_t c0 = e0 < E ? eoff[e0] : 0u;
+    const uint32_t c1 = e1 < E ? eoff[e1] : 0u;
     uint32_t total = 0u;
-    const uint32_t ex = block_exclusive_scan<kDecodeThreads>(c0 + c1, wave_tot, &total);
+    const uint32_t ex = block_exclusive_scan<kLpThreads>(c0 + c1, wave_tot, &total);
     if (e0 < E)
         eoff[e0] = ex;
     if (e1 < E)
@@ -1202,13 +1217,14 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_pack(DecodePlan dp, C
     if (tid == 0)
         eoff[E] = total;
     __syncthreads();
+    const bool exact = repeated != 0u;                   // uniform over the grid
     if (blockIdx.x == 0) {
         const int epr = E / co.N;
-        for (int e = tid; e < E; e += kDecodeThreads) {
+        for (int e = tid; e < E; e += kLpThreads) {
             co.expert_offsets[e] = (int32_t)eoff[e];
             co.expert_counts[e] = (int32_t)(eoff[e + 1] - eoff[e]);
         }
-        for (int r = tid; r < co.N; r += kDecodeThreads) {
+        for (int r = tid; r < co.N; r += kLpThreads) {
             co.rank_offsets[r] = (int32_t)eoff[r * epr];
             co.rank_counts[r] = (int32_t)(eoff[(r + 1) * epr] - eoff[r * epr]);
         }
@@ -1221,57 +1237,65 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_pack(DecodePlan dp, C
     // the wavefront's units; no barrier from here on
     for (bool first = true; u < units; u += waves, first = false) {
         if (!first) {
-            t = u / dp.pieces;
-            c = (int)(u - t * dp.pieces) * 64 + lane;
-            if (c < dp.chunks) {
-                if constexpr (MODE == DECODE_COPY)
-                    xv = static_cast<const u32x4*>(dp.x)[t * dp.chunks + c];
-                else if constexpr (MODE == DECODE_FP8_BF16)
-                    Load8<uint16_t>::run(static_cast<const uint16_t*>(dp.x) + t * dp.H + c * 8,
-                                         v);
-                else
-                    Load8<float>::run(static_cast<const float*>(dp.x) + t * dp.H + c * 8, v);
+            t = u / lp.pieces;
+            c = (int)(u - t * lp.pieces) * 64 + lane;
+            if (c < lp.chunks) {
+                lp_load<MODE>(lp, t, c, xv, v);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     v[i] = 0.0f;
             }
-            id = lane < k ? dp.topk_idx[t * k + lane] : -1;
+            id = lane < k ? lp.topk_idx[t * k + lane] : -1;
         }
+        // an item's own slot is among its expert's count, so every row is below eoff[e + 1] <= R
         int32_t row = -1;
-        if ((uint32_t)id < (uint32_t)E) {
-            // the token's own bit is set in the mask, so row < eoff[id + 1] <= R
-            const int tw = (int)(t >> 5);
-            uint32_t r = eoff[id];
-            for (int w = 0; w < tw; ++w)
-                r += (uint32_t)__popc(mask[w * E + id]);
-            r += (uint32_t)__popc(mask[tw * E + id] & ((1u << (t & 31)) - 1u));
-            row = (int32_t)r;
+        if (!exact) {
+            if ((uint32_t)id < (uint32_t)E) {
+                const int tw = (int)(t >> 5);
+                uint32_t r = eoff[id];
+                for (int w = 0; w < tw; ++w)
+                    r += (uint32_t)__popc(mask[w * E + id]);
+                r += (uint32_t)__popc(mask[tw * E + id] & ((1u << (t & 31)) - 1u));
+                row = (int32_t)r;
+            }
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int32_t ej = __builtin_amdgcn_readlane(id, j);
+                if ((uint32_t)ej >= (uint32_t)E)
+                    continue;                            // uniform per wavefront
+                uint32_t n = 0u;
+                for (int64_t q = lane; q < t * k + j; q += 64)
+                    n += lp.topk_idx[q] == ej ? 1u : 0u;
+                n = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan_u32(n), 63);
+                if (lane == j)
+                    row = (int32_t)(eoff[ej] + n);
+            }
         }
         if (c < 64 && lane < k) {                        // piece 0: the row maps
-            dp.token_row[t * k + lane] = row;
+            lp.token_row[t * k + lane] = row;
             if (row >= 0)
-                dp.row_token[row] = (int32_t)t;
+                lp.row_token[row] = (int32_t)t;
         }
-        const bool active = c < dp.chunks;
-        if constexpr (MODE == DECODE_COPY) {
-            u32x4* rv = static_cast<u32x4*>(dp.recv);
+        const bool active = c < lp.chunks;
+        if constexpr (MODE == LP_COPY) {
+            u32x4* rv = static_cast<u32x4*>(lp.recv);
             for (int j = 0; j < k; ++j) {
                 const int32_t rj = __builtin_amdgcn_readlane(row, j);
                 if (rj >= 0 && active)
-                    __builtin_nontemporal_store(xv, rv + (int64_t)rj * dp.chunks + c);
+                    __builtin_nontemporal_store(xv, rv + (int64_t)rj * lp.chunks + c);
             }
-        } else {
+        } else if constexpr (MODE == LP_FP8_BF16 || MODE == LP_FP8_F32) {
             u32x2 packed;
             const float s = quantise8_e4m3(v, packed);
-            uint8_t* rv = static_cast<uint8_t*>(dp.recv);
+            uint8_t* rv = static_cast<uint8_t*>(lp.recv);
             for (int j = 0; j < k; ++j) {
                 const int32_t rj = __builtin_amdgcn_readlane(row, j);
                 if (rj >= 0 && active) {
                     __builtin_nontemporal_store(
-                        packed, reinterpret_cast<u32x2*>(rv + (int64_t)rj * dp.H) + c);
+                        packed, reinterpret_cast<u32x2*>(rv + (int64_t)rj * lp.H) + c);
                     if ((lane & 15) == 0)
-                        dp.recv_scales[(int64_t)rj * (dp.H / 128) + c / 16] = s;
+                        lp.recv_scales[(int64_t)rj * (lp.H / 128) + c / 16] = s;
                 }
             }
         }
@@ -1902,46 +1926,51 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
                                                                pp, rv, recv_scales);
 }
 
-// Layout and packing of a routed batch in one launch (the ids must be the router's, distinct
-// within a token): up to kDecodeTokens tokens, with the masks and offsets in 64 KB of LDS.
-inline size_t decode_lds_bytes(int32_t T, int32_t E)
+// Layout (and packing, unless payload is null) of a batch in one launch: up to kLpTokens tokens,
+// with the masks and offsets in 64 KB of LDS.
+inline size_t lp_lds_bytes(int32_t T, int32_t E)
 {
     return ((size_t)ceil_div(T, 32) * E + E + 1) * sizeof(uint32_t);
 }
 
-inline bool decode_fits(int32_t T, int32_t E)
+inline bool lp_fits(int32_t T, int32_t E)
 {
-    return T >= 1 && T <= kDecodeTokens && decode_lds_bytes(T, E) <= 64 * 1024;
+    return T >= 1 && T <= kLpTokens && lp_lds_bytes(T, E) + 256 <= 64 * 1024;   // + static LDS
 }
 
-void launch_decode_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t E,
-                        int32_t k, const int32_t* topk_idx, moe_dtype_t payload_dtype,
+void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t E,
+                        int32_t k, const int32_t* topk_idx, const moe_dtype_t* payload_dtype,
                         const moe_dispatch_out_t* out, const CountOutputs& co, hipStream_t stream)
 {
-    const bool fp8 = payload_dtype == MOE_FP8_E4M3;
-    DecodePlan dp;
-    dp.x = x;
-    dp.topk_idx = topk_idx;
-    dp.token_row = out->token_row;
-    dp.row_token = out->row_token;
-    dp.recv = out->recv;
-    dp.recv_scales = out->recv_scales;
-    dp.T = T;
-    dp.k = k;
-    dp.E = E;
-    dp.H = H;
-    dp.words = (int32_t)ceil_div(T, 32);
-    dp.chunks = fp8 ? H / 8 : (int32_t)((int64_t)H * (int64_t)dtype_size(x_dtype) / 16);
-    dp.pieces = (int32_t)ceil_div(dp.chunks, 64);
-    const int64_t groups = ceil_div((int64_t)T * dp.pieces, kDecodeWaves);
-    const dim3 grid((unsigned)(groups < kDecodeMaxGroups ? groups : kDecodeMaxGroups));
-    const size_t lds = decode_lds_bytes(T, E);
-    if (!fp8)
-        k_decode_pack<DECODE_COPY><<<grid, kDecodeThreads, lds, stream>>>(dp, co);
+    const bool layout_only = payload_dtype == nullptr;
+    const bool fp8 = !layout_only && *payload_dtype == MOE_FP8_E4M3;
+    LayoutPackPlan lp;
+    lp.x = x;
+    lp.topk_idx = topk_idx;
+    lp.token_row = out->token_row;
+    lp.row_token = out->row_token;
+    lp.recv = layout_only ? nullptr : out->recv;
+    lp.recv_scales = layout_only ? nullptr : out->recv_scales;
+    lp.T = T;
+    lp.k = k;
+    lp.E = E;
+    lp.H = H;
+    lp.words = (int32_t)ceil_div(T, 32);
+    lp.chunks = layout_only ? 0
+                : fp8       ? H / 8
+                            : (int32_t)((int64_t)H * (int64_t)dtype_size(x_dtype) / 16);
+    lp.pieces = layout_only ? 1 : (int32_t)ceil_div(lp.chunks, 64);
+    const int64_t groups = ceil_div((int64_t)T * lp.pieces, kLpWaves);
+    const dim3 grid((unsigned)(groups < kLpMaxGroups ? groups : kLpMaxGroups));
+    const size_t lds = lp_lds_bytes(T, E);
+    if (layout_only)
+        k_layout_pack<LP_LAYOUT><<<grid, kLpThreads, lds, stream>>>(lp, co);
+    else if (!fp8)
+        k_layout_pack<LP_COPY><<<grid, kLpThreads, lds, stream>>>(lp, co);
     else if (x_dtype == MOE_F32)
-        k_decode_pack<DECODE_FP8_F32><<<grid, kDecodeThreads, lds, stream>>>(dp, co);
+        k_layout_pack<LP_FP8_F32><<<grid, kLpThreads, lds, stream>>>(lp, co);
     else
-        k_decode_pack<DECODE_FP8_BF16><<<grid, kDecodeThreads, lds, stream>>>(dp, co);
+        k_layout_pack<LP_FP8_BF16><<<grid, kLpThreads, lds, stream>>>(lp, co);
 }
 
 template <typename YT, typename OT>
@@ -2014,6 +2043,11 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, 
         return MOE_ERR_WORKSPACE;
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
+    if (lp_fits(T, E)) {
+        launch_layout_pack(nullptr, MOE_F32, T, 0, E, k, topk_idx, nullptr, out,
+                           count_outputs(out, n_ranks), stream);
+        return launch_status();
+    }
     const int64_t R = (int64_t)T * k;
     const LayoutPlan plan = hist_plan(R);
     const Workspace ws = carve_workspace(workspace, T, E, k);
@@ -2055,6 +2089,11 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
         return MOE_ERR_WORKSPACE;
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
+    if (lp_fits(T, E)) {
+        launch_layout_pack(x, x_dtype, T, H, E, k, topk_idx, &payload_dtype, out,
+                           count_outputs(out, n_ranks), stream);
+        return launch_status();
+    }
     const int64_t R = (int64_t)T * k;
     const LayoutPlan plan = hist_plan(R);
     const Workspace ws = carve_workspace(workspace, T, E, k);
@@ -2088,10 +2127,10 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)T * k;
-    if (decode_fits(T, E)) {
-        // decode sizes: routing, then layout and packing in one launch
+    if (lp_fits(T, E)) {
+        // small batches: routing, then layout and packing in one launch
         launch_route(logits, T, E, k, topk_idx, topk_w, stream);
-        launch_decode_pack(x, x_dtype, T, H, E, k, topk_idx, payload_dtype, out,
+        launch_layout_pack(x, x_dtype, T, H, E, k, topk_idx, &payload_dtype, out,
                            count_outputs(out, n_ranks), stream);
         return launch_status();
     }

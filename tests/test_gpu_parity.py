@@ -238,18 +238,27 @@ def test_all_tokens_on_one_expert_and_ties(T):
         _check_payload(buf, d, "f32")
 
 
-def test_duplicate_expert_ids_in_a_token():
-    T, H, E, k, N = 600, 128, 16, 4, 4
-    _announce("edge duplicate ids")
-    rng = np.random.default_rng(1)
+@pytest.mark.parametrize("T,H,E,k,N,payload", [
+    (600, 128, 16, 4, 4, "f32"),       # multi-launch layout
+    (300, 128, 16, 4, 4, "f32"),       # one-launch layout, exact ranks
+    (37, 256, 8, 8, 2, "fp8_e4m3"),    # one-launch layout, k = E with repeats, fp8 from fp32
+    (512, 64, 256, 3, 8, "f32"),       # one-launch layout at its token limit, few repeats
+])
+def test_duplicate_expert_ids_in_a_token(T, H, E, k, N, payload):
+    _announce(f"edge duplicate ids T={T} E={E} k={k} payload={payload}")
+    rng = np.random.default_rng(T + E)
     idx = rng.integers(0, E, (T, k)).astype(np.int32)          # repeats allowed
     x = rng.standard_normal((T, H)).astype(np.float32)
-    d = oracle.dispatch(x, "f32", idx, E, N, "f32")
-    buf = moe.alloc_dispatch_out(T, H, E, k, N, "f32")
+    d = oracle.dispatch(x, "f32", idx, E, N, payload)
+    buf = moe.alloc_dispatch_out(T, H, E, k, N, payload)
     moe.moe_dispatch(to_dev(x, "f32"), to_dev(idx, "i32"), E, N, buf, moe.alloc_workspace(T, E, k))
+    lay = moe.alloc_dispatch_out(T, H, E, k, N, None)
+    moe.moe_dispatch_layout(to_dev(idx, "i32"), E, N, lay, moe.alloc_workspace(T, E, k))
     torch.cuda.synchronize()
+    assert oracle.check_topk(idx, E)[1] > 0
     _check_layout(buf, d)
-    _check_payload(buf, d, "f32")
+    _check_layout(lay, d)
+    _check_payload(buf, d, payload)
 
 
 def test_fp8_special_blocks():
@@ -294,10 +303,11 @@ def test_zero_tokens_writes_zero_counts():
         assert np.all(to_host(t) == 0)
 
 
-def test_out_of_range_ids_are_skipped_and_nothing_outside_is_written():
+@pytest.mark.parametrize("T", [50, 700])
+def test_out_of_range_ids_are_skipped_and_nothing_outside_is_written(T):
     """Ids outside [0, E) get token_row -1 and no row; canaries after every buffer stay intact."""
-    T, H, E, k, N = 50, 256, 8, 2, 2
-    _announce("edge out-of-range ids + canaries")
+    H, E, k, N = 256, 8, 2, 2
+    _announce(f"edge out-of-range ids + canaries T={T}")
     rng = np.random.default_rng(3)
     idx = random_topk(T, E, k, 3)
     idx[4, 1] = E

@@ -40,6 +40,9 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="prefill")
+    p.add_argument("--settle-seconds", type=float, default=0.3,
+                   help="before the warmup steps, run the plain copy kernel this long so the GPU "
+                        "reaches its steady clocks (0 disables it)")
     p.add_argument("--sets", type=int, default=2,
                    help="buffer sets used in rotation (each set is about 1 GB at prefill)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -158,6 +161,28 @@ def copy_ceiling(torch, gib: float = 1.0, iters: int = 10):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     return {"bytes_per_launch": 2 * n, "us": ms * 1e3, "GBps": 2 * n / (ms * 1e-3) / 1e9}
+
+
+def settle_clocks(torch, seconds: float) -> float:
+    """Run the plain copy kernel over 256 MiB for about `seconds` of wall time, so that the timed
+    loop does not start while the GPU is still raising its clocks; returns the seconds spent."""
+    if seconds <= 0:
+        return 0.0
+    from combine_moe_route_03_amd import build as b
+    lib = ctypes.CDLL(b.BENCH_LIB)
+    lib.bench_stream_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p]
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            assert lib.bench_stream_copy16(src.data_ptr(), dst.data_ptr(), n, stream) == 0
+        torch.cuda.synchronize()
+    del src, dst
+    return time.perf_counter() - t0
 
 
 def hbm_traffic(kernel_pattern: str):
@@ -454,6 +479,7 @@ def main():
     headline = HEADLINE
     separate = ("route", "dispatch", "combine")
     split = ("route", "layout", "pack", "combine")
+    settled_s = settle_clocks(torch, args.settle_seconds)
     for i in range(args.warmup):
         for ph in headline:
             sets[i % len(sets)][ph]()
@@ -552,6 +578,7 @@ def main():
         "other_workloads": others,
         "ep_emulation": ep,
         "wall_s_timed_loop": round(wall, 4),
+        "clock_settle_s": round(settled_s, 3),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

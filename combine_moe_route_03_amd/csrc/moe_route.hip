@@ -1141,7 +1141,24 @@ struct LayoutPackPlan {
     int32_t words;        // ceil(T / 32) mask words per expert
     int32_t chunks;       // lane chunks per row: 16 bytes (copy) or 8 elements (fp8); 0 for layout
     int32_t pieces;       // ceil(chunks / 64), at least 1
+    // expert-parallel send (ep_L > 0): rows go to the regions of this source, as in k_layout_rows
+    int32_t* ep_counts;
+    int32_t ep_source, ep_sources, ep_cap, ep_L;
 };
+
+// Row of an item of expert e (in range) with rank `rank` among the expert's items: the packed row,
+// or for an expert-parallel send the row in region (rank of e, source), -1 past the region.
+__device__ __forceinline__ int32_t lp_row(const LayoutPackPlan& lp, const uint32_t* eoff, int32_t e,
+                                          uint32_t rank)
+{
+    if (lp.ep_L == 0)
+        return (int32_t)(eoff[e] + rank);
+    const int32_t r = e / lp.ep_L;
+    const uint32_t pos = eoff[e] - eoff[r * lp.ep_L] + rank;
+    return pos < (uint32_t)lp.ep_cap
+               ? (int32_t)(((int64_t)r * lp.ep_sources + lp.ep_source) * lp.ep_cap + pos)
+               : -1;
+}
 
 template <int MODE>
 __device__ __forceinline__ void lp_load(const LayoutPackPlan& lp, int64_t t, int c, u32x4& xv,
@@ -1218,7 +1235,11 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
         eoff[E] = total;
     __syncthreads();
     const bool exact = repeated != 0u;                   // uniform over the grid
-    if (blockIdx.x == 0) {
+    if (blockIdx.x == 0 && lp.ep_L > 0) {
+        for (int e = tid; e < E; e += kLpThreads)
+            lp.ep_counts[((int64_t)(e / lp.ep_L) * lp.ep_sources + lp.ep_source) * lp.ep_L +
+                         e % lp.ep_L] = (int32_t)(eoff[e + 1] - eoff[e]);
+    } else if (blockIdx.x == 0) {
         const int epr = E / co.N;
         for (int e = tid; e < E; e += kLpThreads) {
             co.expert_offsets[e] = (int32_t)eoff[e];
@@ -1248,16 +1269,17 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
             }
             id = lane < k ? lp.topk_idx[t * k + lane] : -1;
         }
-        // an item's own slot is among its expert's count, so every row is below eoff[e + 1] <= R
+        // an item's own slot is among its expert's count, so its rank is below that count and
+        // every packed row is below eoff[e + 1] <= R
         int32_t row = -1;
         if (!exact) {
             if ((uint32_t)id < (uint32_t)E) {
                 const int tw = (int)(t >> 5);
-                uint32_t r = eoff[id];
+                uint32_t r = 0u;
                 for (int w = 0; w < tw; ++w)
                     r += (uint32_t)__popc(mask[w * E + id]);
                 r += (uint32_t)__popc(mask[tw * E + id] & ((1u << (t & 31)) - 1u));
-                row = (int32_t)r;
+                row = lp_row(lp, eoff, id, r);
             }
         } else {
             for (int j = 0; j < k; ++j) {
@@ -1269,12 +1291,12 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
                     n += lp.topk_idx[q] == ej ? 1u : 0u;
                 n = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan_u32(n), 63);
                 if (lane == j)
-                    row = (int32_t)(eoff[ej] + n);
+                    row = lp_row(lp, eoff, ej, n);
             }
         }
         if (c < 64 && lane < k) {                        // piece 0: the row maps
             lp.token_row[t * k + lane] = row;
-            if (row >= 0)
+            if (row >= 0 && lp.row_token)
                 lp.row_token[row] = (int32_t)t;
         }
         const bool active = c < lp.chunks;
@@ -1940,7 +1962,8 @@ inline bool lp_fits(int32_t T, int32_t E)
 
 void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t E,
                         int32_t k, const int32_t* topk_idx, const moe_dtype_t* payload_dtype,
-                        const moe_dispatch_out_t* out, const CountOutputs& co, hipStream_t stream)
+                        const moe_dispatch_out_t* out, const CountOutputs& co, hipStream_t stream,
+                        const EpSend* ep = nullptr)
 {
     const bool layout_only = payload_dtype == nullptr;
     const bool fp8 = !layout_only && *payload_dtype == MOE_FP8_E4M3;
@@ -1960,6 +1983,11 @@ void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H
                 : fp8       ? H / 8
                             : (int32_t)((int64_t)H * (int64_t)dtype_size(x_dtype) / 16);
     lp.pieces = layout_only ? 1 : (int32_t)ceil_div(lp.chunks, 64);
+    lp.ep_counts = ep ? ep->counts : nullptr;
+    lp.ep_source = ep ? ep->source : 0;
+    lp.ep_sources = ep ? ep->sources : 1;
+    lp.ep_cap = ep ? ep->cap : 0;
+    lp.ep_L = ep ? ep->L : 0;
     const int64_t groups = ceil_div((int64_t)T * lp.pieces, kLpWaves);
     const dim3 grid((unsigned)(groups < kLpMaxGroups ? groups : kLpMaxGroups));
     const size_t lds = lp_lds_bytes(T, E);
@@ -2259,6 +2287,14 @@ moe_status_t moe_ep_send(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t 
     ep.sources = n_sources;
     ep.cap = cap;
     ep.L = E / n_ranks;
+    if (lp_fits(T, E)) {
+        moe_dispatch_out_t o = {};
+        o.recv = regions;
+        o.token_row = send_row;
+        launch_layout_pack(x, x_dtype, T, H, E, k, topk_idx, &x_dtype, &o, CountOutputs{}, stream,
+                           &ep);
+        return launch_status();
+    }
     launch_hist(topk_idx, R, E, ws, plan, stream);
     const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
     const CountOutputs none = {};

@@ -94,9 +94,13 @@ def _run(w: EpWorkload, sample_rows: int = 0):
                 o_rows=o_rows, idx=idx, wt=wt, o_out=o_out)
 
 
-@pytest.mark.parametrize("name", ["ep_tiny", "ep_decode"])
+# more tokens per source than the one-launch layout takes: the multi-launch region layout
+EP_WIDE = EpWorkload("ep_wide", 3, 700, 256, 64, 4, 8, "bf16")
+
+
+@pytest.mark.parametrize("name", ["ep_tiny", "ep_decode", "ep_wide"])
 def test_ep_send_recv_return_combine(name):
-    w = EP_WORKLOADS[name]
+    w = EP_WORKLOADS.get(name) or EP_WIDE
     _announce(f"ep {name} S={w.S} T={w.T} H={w.H} E={w.E} k={w.k} N={w.N} cap={w.cap}")
     _run(w)
 

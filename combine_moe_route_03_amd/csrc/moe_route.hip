@@ -52,7 +52,7 @@ constexpr int kRouteTokens16 = kThreads / 16;   // route-layout workgroup, k <= 
 constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
 constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
 constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
-constexpr int kCombineWaves = 2;         // wavefronts per combine workgroup
+constexpr int kCombineWaves = 1;         // wavefronts per combine workgroup
 constexpr int kXcds = 8;
 constexpr int kLpTokens = 512;           // layout folded into packing: at most this many tokens
 constexpr int kLpThreads = 512;          //   (8 wavefronts a workgroup, two experts a thread)

@@ -50,7 +50,8 @@ constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kRouteTokens = kGroupWaves;   // route-layout workgroup, k > 16: a token a wave
 constexpr int kRouteTokens16 = kThreads / 16;   // route-layout workgroup, k <= 16: 16 lanes each
 constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
-constexpr int kPackWaves = 16;           // wavefronts per pack workgroup
+constexpr int kPackWaves = 16;           // wavefronts per pack / copy workgroup
+constexpr int kPackWavesWindows = 8;     //   (8 for the window-ordered pack)
 constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
 constexpr int kCombineWaves = 1;         // wavefronts per combine workgroup
 constexpr int kXcds = 8;
@@ -904,6 +905,13 @@ __device__ __forceinline__ XcdItem xcd_item(int waves_per_group, int items_per_t
 // out in ascending order, which keeps the writes of the whole GPU in a narrow address range.
 enum PackOrder { PACK_TOKEN_ORDER = 0, PACK_WINDOWS = 1 };
 
+// Wavefronts per packing workgroup: 16 in token order, 8 in window order (each measured best).
+template <int ORDER>
+constexpr int pack_waves()
+{
+    return ORDER == PACK_WINDOWS ? kPackWavesWindows : kPackWaves;
+}
+
 struct PackPlan {
     const int32_t* token_row;
     const int2* list;
@@ -931,7 +939,7 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
     it.row = -1;
     it.piece = 0;
     if constexpr (ORDER == PACK_TOKEN_ORDER) {
-        const XcdItem xi = xcd_item(kPackWaves, pp.k * pp.pieces);
+        const XcdItem xi = xcd_item(pack_waves<ORDER>(), pp.k * pp.pieces);
         if (xi.token < pp.T) {
             const int j = xi.sub / pp.pieces;
             it.piece = xi.sub - j * pp.pieces;
@@ -939,7 +947,7 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
             it.token = xi.token;
         }
     } else {
-        const XcdItem xi = xcd_item(kPackWaves, pp.rows_per_window * pp.pieces);
+        const XcdItem xi = xcd_item(pack_waves<ORDER>(), pp.rows_per_window * pp.pieces);
         const int q = xi.sub / pp.pieces;
         const int64_t pos = xi.token * pp.rows_per_window + q;   // "token" is the window here
         if (xi.token < pp.nwin && pos < pp.R) {
@@ -959,10 +967,8 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
 // wavefronts that copy the same token find it in L2. The pieces of a row run side by side. A row
 // outside [0, R) is skipped.
 template <int ORDER>
-__global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows(const u32x4* __restrict__ x,
-                                                               int32_t chunks_per_row,
-                                                               PackPlan pp,
-                                                               u32x4* __restrict__ recv)
+__global__ __launch_bounds__(64 * pack_waves<ORDER>()) void k_pack_rows(
+    const u32x4* __restrict__ x, int32_t chunks_per_row, PackPlan pp, u32x4* __restrict__ recv)
 {
     const PackItem it = pack_item<ORDER>(pp);
     if (it.token < 0)
@@ -1924,20 +1930,23 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
     pp.nwin = wp ? wp->nwin : 0;
     pp.row_limit = row_limit;
     const bool windows = wp && (int64_t)pp.rows_per_window * pp.pieces < (int64_t)INT32_MAX / 2;
-    const dim3 grid((unsigned)(windows ? xcd_blocks(pp.nwin, (int64_t)pp.rows_per_window *
-                                                                 pp.pieces, kPackWaves)
-                                       : xcd_blocks(T, (int64_t)k * pp.pieces, kPackWaves)));
-    const dim3 block(64 * kPackWaves);
     const u32x4* xs = static_cast<const u32x4*>(x);
     if (!fp8) {
         u32x4* rv = static_cast<u32x4*>(recv);
-        if (windows)
-            k_pack_rows<PACK_WINDOWS><<<grid, block, 0, stream>>>(xs, cpr, pp, rv);
-        else
-            k_pack_rows<PACK_TOKEN_ORDER><<<grid, block, 0, stream>>>(xs, cpr, pp, rv);
+        if (windows) {
+            constexpr int wpg = pack_waves<PACK_WINDOWS>();
+            const dim3 grid((unsigned)xcd_blocks(pp.nwin, (int64_t)pp.rows_per_window * pp.pieces,
+                                                 wpg));
+            k_pack_rows<PACK_WINDOWS><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
+        } else {
+            constexpr int wpg = pack_waves<PACK_TOKEN_ORDER>();
+            const dim3 grid((unsigned)xcd_blocks(T, (int64_t)k * pp.pieces, wpg));
+            k_pack_rows<PACK_TOKEN_ORDER><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
+        }
         return;
     }
     // fp8: one wavefront per (token, piece), quantised once and stored to the token's k rows
+    const dim3 block(64 * kPackWaves);
     const dim3 grid8((unsigned)xcd_blocks(T, pp.pieces, kPackWaves));
     uint8_t* rv = static_cast<uint8_t*>(recv);
     if (x_dtype == MOE_F32)

@@ -1677,10 +1677,10 @@ inline Workspace carve_workspace(void* base, int32_t T, int32_t E, int32_t k)
 }
 
 // Packing windows: about as many layout blocks as keep the window's x rows within kWindowBytes
-// (they stay in one XCD's L2 while the window is packed, with room to spare for what earlier
-// kernels left there), with the window count rounded up to a multiple of 8 so that every XCD gets
-// the same number of windows. x_row_bytes = 0 (no packing follows) takes 8 windows.
-constexpr int64_t kWindowBytes = 1792 * 1024;
+// (they stay in the 4 MB L2 of one XCD while the window is packed), with the window count rounded
+// up to a multiple of 8 so that every XCD gets the same number of windows where the block count
+// allows it. x_row_bytes = 0 (no packing follows) takes 8 windows.
+constexpr int64_t kWindowBytes = 3584 * 1024;
 
 struct WindowPlan {
     int32_t blocks_per_window;

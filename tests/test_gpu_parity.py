@@ -301,6 +301,34 @@ def test_zero_tokens_writes_zero_counts():
     torch.cuda.synchronize()
     for t in (buf.expert_counts, buf.expert_offsets, buf.rank_counts, buf.rank_offsets):
         assert np.all(to_host(t) == 0)
+        t.fill_(-7)
+    ids0 = torch.empty((0, k), dtype=torch.int32, device="cuda")
+    moe.moe_dispatch_layout(ids0, E, N, buf, moe.alloc_workspace(0, E, k))
+    torch.cuda.synchronize()
+    for t in (buf.expert_counts, buf.expert_offsets, buf.rank_counts, buf.rank_offsets):
+        assert np.all(to_host(t) == 0)
+    # the calls with nothing to count enqueue nothing and return OK
+    x0 = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    moe.moe_route_topk(torch.empty((0, E), dtype=torch.float32, device="cuda"), k)
+    moe.moe_dispatch_pack(x0, k, buf.token_row, buf.recv)
+    moe.moe_combine(torch.empty((0, 128), dtype=torch.bfloat16, device="cuda"), buf.token_row,
+                    torch.empty((0, k), dtype=torch.float32, device="cuda"), x0)
+    # expert-parallel halves: an empty source publishes zero counts in its own column only
+    S, src = 3, 1
+    L = E // N
+    cap = moe.moe_ep_capacity(0, E, k, N)
+    regions = torch.zeros((max(N * S * cap, 1), 128), dtype=torch.bfloat16, device="cuda")
+    rcounts = torch.full((N, S, L), -7, dtype=torch.int32, device="cuda")
+    moe.moe_ep_send(x0, ids0, E, N, src, S, cap, regions, rcounts,
+                    torch.empty(0, dtype=torch.int32, device="cuda"), moe.alloc_workspace(0, E, k))
+    pcounts = torch.full((N, S), -7, dtype=torch.int32, device="cuda")
+    moe.moe_ep_partial_rows(ids0, E, N, src, S, 0, torch.empty((0, N), dtype=torch.int32,
+                                                               device="cuda"), pcounts)
+    torch.cuda.synchronize()
+    rc = to_host(rcounts)
+    assert np.all(rc[:, src, :] == 0) and np.all(np.delete(rc, src, axis=1) == -7)
+    pc = to_host(pcounts)
+    assert np.all(pc[:, src] == 0) and np.all(np.delete(pc, src, axis=1) == -7)
 
 
 @pytest.mark.parametrize("T", [50, 700])

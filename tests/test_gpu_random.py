@@ -1,0 +1,81 @@
+"""Seeded random shapes through moe_route_dispatch, moe_dispatch (caller ids, some with repeats)
+and moe_combine, against the oracle. Shapes cross the one-launch layout's limits (512 tokens, 64 KB
+of masks), ragged rows and pieces, E up to 1024 and k up to 64; every output is compared bit for
+bit (combine to one bf16 code / 1e-5 relative)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_route_03_amd import _lib as moe
+from combine_moe_route_03_amd.workloads import Workload, make_inputs
+from gpu_util import assert_close_out, to_dev, to_host
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+LAYOUT = ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "token_row",
+          "row_token")
+
+
+def _shape(case: int):
+    rng = np.random.default_rng(1000 + case)
+    T = int(rng.choice([1, 2, 31, 33, 64, 127, 200, 255, 300, 448, 511, 512, 513, 700, 1100]))
+    N = int(rng.choice([1, 2, 4, 8, 16]))
+    E = N * int(rng.integers(1, max(2, 1024 // N) + 1))
+    E = min(E, 1024)
+    k = int(rng.integers(1, min(E, 64) + 1))
+    x_dtype = str(rng.choice(["f32", "bf16"]))
+    payload = str(rng.choice([x_dtype, "fp8_e4m3"]))
+    if payload == "fp8_e4m3":
+        H = 128 * int(rng.integers(1, 5))
+    else:
+        H = 8 * int(rng.integers(1, 200))
+        if x_dtype == "bf16" and H % 8:
+            H += 8 - H % 8
+    while T * k * H > 3_000_000 and H > 128:       # keep the oracle quick
+        H = max(128 if payload == "fp8_e4m3" else 8, (H // 2) // 8 * 8)
+    if payload == "fp8_e4m3":
+        H = max(128, H // 128 * 128)
+    return T, H, E, k, N, x_dtype, payload, rng
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_shape_matches_oracle(case):
+    T, H, E, k, N, x_dtype, payload, rng = _shape(case)
+    print(f"[gpu] random case {case}: T={T} H={H} E={E} k={k} N={N} x={x_dtype} "
+          f"payload={payload}", flush=True)
+    w = Workload("rand", T, H, E, k, N, x_dtype, payload, x_dtype, x_dtype, "scale",
+                 seed=case)
+    inp = make_inputs(w)
+    idx, wt = oracle.route(inp["logits"], k)
+    d = oracle.dispatch(inp["x"], x_dtype, idx, E, N, payload)
+    buf = moe.alloc_dispatch_out(T, H, E, k, N, payload)
+    ws = moe.alloc_workspace(T, E, k)
+    g_idx, g_w, _ = moe.moe_route_dispatch(to_dev(inp["logits"], "f32"),
+                                           to_dev(inp["x"], x_dtype), k, N, buf, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(g_idx), idx)
+    g_w = to_host(g_w).astype(np.float64)
+    assert np.all(np.abs(g_w - wt) <= 1e-6 * np.abs(wt))
+    for key in LAYOUT:
+        assert np.array_equal(to_host(getattr(buf, key)), d[key]), key
+    assert np.array_equal(to_host(buf.recv), d["recv"])
+    if payload == "fp8_e4m3":
+        assert np.array_equal(to_host(buf.recv_scales), d["recv_scales"])
+    y_dtype = "bf16" if payload == "fp8_e4m3" else x_dtype
+    y = oracle.experts(d["recv"], payload, d["recv_scales"], d["expert_offsets"], "scale", y_dtype)
+    out = torch.empty((T, H), dtype=moe.TORCH_DTYPES[x_dtype], device="cuda")
+    moe.moe_combine(to_dev(y, y_dtype), buf.token_row, to_dev(wt, "f32"), out)
+    torch.cuda.synchronize()
+    assert_close_out(to_host(out), oracle.combine(y, y_dtype, d["token_row"], wt, x_dtype),
+                     x_dtype)
+    if case % 4 == 0:                               # caller-given ids with repeats
+        ids = rng.integers(0, E, (T, k)).astype(np.int32)
+        d2 = oracle.dispatch(inp["x"], x_dtype, ids, E, N, payload)
+        buf2 = moe.alloc_dispatch_out(T, H, E, k, N, payload)
+        moe.moe_dispatch(to_dev(inp["x"], x_dtype), to_dev(ids, "i32"), E, N, buf2, ws)
+        torch.cuda.synchronize()
+        for key in LAYOUT:
+            assert np.array_equal(to_host(getattr(buf2, key)), d2[key]), key
+        assert np.array_equal(to_host(buf2.recv), d2["recv"])

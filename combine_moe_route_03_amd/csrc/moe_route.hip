@@ -29,8 +29,9 @@
 //                    and packs its pieces, so layout and packing take one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
 //                    fp32 fused multiply-adds, one 16-byte store per 8 outputs;
-//   k_ep_recv_plan   expert-parallel receive: one workgroup turns a rank's per-(source, expert)
-//                    region counts into the grouped layout and each grouped row's region row;
+//   k_ep_recv_plan   expert-parallel receive: every workgroup scans a rank's per-(source, expert)
+//                    region counts into the grouped layout and finds the region row of its share
+//                    of the grouped rows;
 //   k_copy_rows      grid-stride row gather / scatter by a row map (expert-parallel receive and
 //                    the return half of combine);
 //   k_ep_partial_rows, k_ep_invert, k_ep_reduce, k_ep_finish  combine with pre-reduction on the

@@ -502,7 +502,9 @@ def main():
     # which is what a kernel trace averages.
     kernel_us = {ph: timed(torch, sets, (ph,), K, False)[0] * 1e3 for ph in ("pack", "combine")}
     dominant = max(kernel_us, key=lambda ph: kernel_us[ph])
-    pattern = {"pack": r"k_pack_rows(_fp8)?<(.*, )?0>", "combine": r"k_combine<.*>"}[dominant]
+    # the pack timed alone is the token-order form: k_pack_rows<0, 1> (order 0, one piece a wave)
+    pattern = {"pack": r"k_pack_rows<0, 1>|k_pack_rows_fp8<.*>",
+               "combine": r"k_combine<.*>"}[dominant]
     prof_name, traffic = hbm_traffic(pattern)
     kernel_name = prof_name or {"pack": "k_pack_rows" if w.payload != "fp8_e4m3"
                                 else "k_pack_rows_fp8", "combine": "k_combine"}[dominant]

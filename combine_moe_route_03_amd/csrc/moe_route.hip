@@ -53,6 +53,7 @@ constexpr int kRouteTokens16 = kThreads / 16;   // route-layout workgroup, k <= 
 constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
 constexpr int kPackWaves = 16;           // wavefronts per pack / copy workgroup
 constexpr int kPackWavesWindows = 8;     //   (8 for the window-ordered pack)
+constexpr int kPackSplitPieces = 12;     // window order: rows of fewer 1 KB pieces take 2 a wave
 constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
 constexpr int kCombineWaves = 1;         // wavefronts per combine workgroup
 constexpr int kXcds = 8;
@@ -917,6 +918,7 @@ struct PackPlan {
     const int32_t* token_row;
     const int2* list;
     int32_t T, k, R, pieces;          // R = T*k items
+    int32_t window_pieces;            // window order: work items per row (pieces / pieces a wave)
     int32_t rows_per_window, nwin;
     int64_t row_limit;                // rows of the destination buffer
 };
@@ -948,11 +950,11 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
             it.token = xi.token;
         }
     } else {
-        const XcdItem xi = xcd_item(pack_waves<ORDER>(), pp.rows_per_window * pp.pieces);
-        const int q = xi.sub / pp.pieces;
+        const XcdItem xi = xcd_item(pack_waves<ORDER>(), pp.rows_per_window * pp.window_pieces);
+        const int q = xi.sub / pp.window_pieces;
         const int64_t pos = xi.token * pp.rows_per_window + q;   // "token" is the window here
         if (xi.token < pp.nwin && pos < pp.R) {
-            it.piece = xi.sub - q * pp.pieces;
+            it.piece = xi.sub - q * pp.window_pieces;
             const int2 rt = pp.list[pos];
             if ((uint64_t)(uint32_t)rt.x < (uint64_t)pp.row_limit && rt.x >= 0) {
                 it.row = rt.x;
@@ -963,25 +965,33 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
     return it;
 }
 
-// One wavefront per (row, 1 KB piece of it): lane l copies chunk piece*64 + l (16 bytes) of x's
-// row to the destination row with a non-temporal store; x is read with plain loads so the
-// wavefronts that copy the same token find it in L2. The pieces of a row run side by side. A row
-// outside [0, R) is skipped.
-template <int ORDER>
+// One wavefront per (row, PPW consecutive 1 KB pieces of it): lane l copies chunks
+// (piece*PPW + p)*64 + l (16 bytes each) of x's row to the destination row with non-temporal
+// stores, all loads issued before the stores; x is read with plain loads so the wavefronts that
+// copy the same token find it in L2. The pieces of a row run side by side. A row outside [0, R) is
+// skipped. PPW > 1 only in window order.
+template <int ORDER, int PPW>
 __global__ __launch_bounds__(64 * pack_waves<ORDER>()) void k_pack_rows(
     const u32x4* __restrict__ x, int32_t chunks_per_row, PackPlan pp, u32x4* __restrict__ recv)
 {
     const PackItem it = pack_item<ORDER>(pp);
     if (it.token < 0)
         return;                                          // uniform per wavefront
-    const int c = it.piece * 64 + (threadIdx.x & 63);
-    const bool active = c < chunks_per_row;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (active)
-        v = x[it.token * chunks_per_row + c];
+    const int c0 = it.piece * (64 * PPW) + (threadIdx.x & 63);
+    u32x4 v[PPW];
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+        v[p] = u32x4{0u, 0u, 0u, 0u};
+        if (c0 + 64 * p < chunks_per_row)
+            v[p] = x[it.token * chunks_per_row + c0 + 64 * p];
+    }
     const int32_t row = ORDER == PACK_TOKEN_ORDER ? pp.token_row[it.index] : it.row;
-    if (active && row >= 0 && (int64_t)row < pp.row_limit)
-        __builtin_nontemporal_store(v, recv + (int64_t)row * chunks_per_row + c);
+    if (row < 0 || (int64_t)row >= pp.row_limit)
+        return;
+#pragma unroll
+    for (int p = 0; p < PPW; ++p)
+        if (c0 + 64 * p < chunks_per_row)
+            __builtin_nontemporal_store(v[p], recv + (int64_t)row * chunks_per_row + c0 + 64 * p);
 }
 
 // Copies of whole rows by a row map, grid-stride over (row, 1 KB piece) by wavefronts: GATHER
@@ -1927,6 +1937,9 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
     pp.k = k;
     pp.R = R;
     pp.pieces = (int32_t)ceil_div(fp8 ? H / 8 : cpr, 64);
+    // window order: rows of fewer than kPackSplitPieces pieces take two pieces a wavefront
+    const bool two = pp.pieces < kPackSplitPieces;
+    pp.window_pieces = two ? (pp.pieces + 1) / 2 : pp.pieces;
     pp.rows_per_window = wp ? wp->rows_per_window : 0;
     pp.nwin = wp ? wp->nwin : 0;
     pp.row_limit = row_limit;
@@ -1936,13 +1949,16 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
         u32x4* rv = static_cast<u32x4*>(recv);
         if (windows) {
             constexpr int wpg = pack_waves<PACK_WINDOWS>();
-            const dim3 grid((unsigned)xcd_blocks(pp.nwin, (int64_t)pp.rows_per_window * pp.pieces,
-                                                 wpg));
-            k_pack_rows<PACK_WINDOWS><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
+            const dim3 grid((unsigned)xcd_blocks(
+                pp.nwin, (int64_t)pp.rows_per_window * pp.window_pieces, wpg));
+            if (two)
+                k_pack_rows<PACK_WINDOWS, 2><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
+            else
+                k_pack_rows<PACK_WINDOWS, 1><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
         } else {
             constexpr int wpg = pack_waves<PACK_TOKEN_ORDER>();
             const dim3 grid((unsigned)xcd_blocks(T, (int64_t)k * pp.pieces, wpg));
-            k_pack_rows<PACK_TOKEN_ORDER><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
+            k_pack_rows<PACK_TOKEN_ORDER, 1><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
         }
         return;
     }

@@ -26,7 +26,8 @@
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
 //   k_layout_pack    batches of up to 512 tokens: every workgroup rebuilds the whole layout in
 //                    LDS from the ids (LDS counts, one block scan, token bit masks for the ranks)
-//                    and packs its pieces, so layout and packing take one launch;
+//                    and packs its pieces, so layout and packing take one launch; up to 32 routed
+//                    tokens every workgroup also routes the batch itself, so dispatch is one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
 //                    fp32 fused multiply-adds, one 16-byte store per 8 outputs;
 //   k_ep_recv_plan   expert-parallel receive: every workgroup scans a rank's per-(source, expert)
@@ -60,7 +61,8 @@ constexpr int kXcds = 8;
 constexpr int kLpTokens = 512;           // layout folded into packing: at most this many tokens
 constexpr int kLpThreads = 512;          //   (8 wavefronts a workgroup, two experts a thread)
 constexpr int kLpWaves = kLpThreads / 64;
-constexpr int kLpMaxGroups = 1024;       //   (grid-stride beyond this many workgroups)                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
+constexpr int kLpMaxGroups = 1024;       //   (grid-stride beyond this many workgroups)
+constexpr int kLpRouteTokens = kLpThreads / 16;   // routing in the same launch: at most 32 tokens                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -469,7 +471,7 @@ __device__ __forceinline__ int route_row16(const float (&v)[P], int32_t E, int32
     sum = dpp_add_f64<kDppQuadXor2>(sum);
     sum = dpp_add_f64<kDppRowHalfMirror>(sum);
     sum = dpp_add_f64<kDppRowMirror>(sum);
-    if (slot) {
+    if (slot && idx_out != nullptr) {                   // null outputs: the ids only
         idx_out[l16] = my_id;
         w_out[l16] = (float)(ex / sum);
     }
@@ -1161,6 +1163,10 @@ struct LayoutPackPlan {
     // expert-parallel send (ep_L > 0): rows go to the regions of this source, as in k_layout_rows
     int32_t* ep_counts;
     int32_t ep_source, ep_sources, ep_cap, ep_L;
+    // routing in the same launch (RP > 0): logits in, ids and weights out (workgroup 0 writes them)
+    const float* logits;
+    int32_t* route_idx;
+    float* route_w;
 };
 
 // Row of an item of expert e (in range) with rank `rank` among the expert's items: the packed row,
@@ -1189,7 +1195,7 @@ __device__ __forceinline__ void lp_load(const LayoutPackPlan& lp, int64_t t, int
         Load8<float>::run(static_cast<const float*>(lp.x) + t * lp.H + c * 8, v);
 }
 
-template <int MODE>
+template <int MODE, int RP>
 __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, CountOutputs co)
 {
     extern __shared__ uint32_t lds_lp[];
@@ -1198,6 +1204,8 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
     const int32_t E = lp.E, W = lp.words, k = lp.k;
     uint32_t* mask = lds_lp;                             // [W][E]
     uint32_t* eoff = lds_lp + (int64_t)W * E;            // [E + 1]: counts, then offsets
+    int32_t* ids = reinterpret_cast<int32_t*>(eoff + E + 1);     // [T * k] when routing here
+    const int32_t* __restrict__ topk_idx = RP > 0 ? ids : lp.topk_idx;
     const int tid = threadIdx.x, lane = tid & 63;
     const int64_t waves = (int64_t)gridDim.x * kLpWaves;
     const int64_t units = (int64_t)lp.T * lp.pieces;
@@ -1215,8 +1223,25 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
     if (u < units) {
         if (c < lp.chunks)
             lp_load<MODE>(lp, t, c, xv, v);
-        if (lane < k)
+        if (RP == 0 && lane < k)
             id = lp.topk_idx[t * k + lane];
+    }
+
+    // routing (RP > 0, at most kLpRouteTokens tokens and k <= 16): every workgroup routes the whole
+    // batch, 16 lanes a token, into LDS; workgroup 0 also writes the ids and weights
+    if constexpr (RP > 0) {
+        const int q = tid >> 4;                          // token, 0 .. kLpThreads / 16 - 1
+        const bool valid = q < lp.T;
+        float lg[RP];
+        load_logits16<RP>(lp.logits + (int64_t)(valid ? q : 0) * E, valid ? E : 0, lg);
+        const bool out = blockIdx.x == 0 && valid;
+        const int my = route_row16<RP>(lg, E, k, valid, out ? lp.route_idx + q * k : nullptr,
+                                       out ? lp.route_w + q * k : nullptr);
+        if (valid && (tid & 15) < k)
+            ids[q * k + (tid & 15)] = my;
+        __syncthreads();
+        if (u < units && lane < k)
+            id = ids[t * k + lane];
     }
 
     // the layout, in every workgroup
@@ -1229,7 +1254,7 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
     __syncthreads();
     const int32_t R = lp.T * k;
     for (int32_t i = tid; i < R; i += kLpThreads) {
-        const int32_t e = lp.topk_idx[i];
+        const int32_t e = topk_idx[i];
         if ((uint32_t)e < (uint32_t)E) {
             const int32_t tt = i / k;
             const uint32_t bit = 1u << (tt & 31);
@@ -1284,7 +1309,7 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
                 for (int i = 0; i < 8; ++i)
                     v[i] = 0.0f;
             }
-            id = lane < k ? lp.topk_idx[t * k + lane] : -1;
+            id = lane < k ? topk_idx[t * k + lane] : -1;
         }
         // an item's own slot is among its expert's count, so its rank is below that count and
         // every packed row is below eoff[e + 1] <= R
@@ -1305,7 +1330,7 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
                     continue;                            // uniform per wavefront
                 uint32_t n = 0u;
                 for (int64_t q = lane; q < t * k + j; q += 64)
-                    n += lp.topk_idx[q] == ej ? 1u : 0u;
+                    n += topk_idx[q] == ej ? 1u : 0u;
                 n = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan_u32(n), 63);
                 if (lane == j)
                     row = lp_row(lp, eoff, ej, n);
@@ -1986,10 +2011,20 @@ inline bool lp_fits(int32_t T, int32_t E)
     return T >= 1 && T <= kLpTokens && lp_lds_bytes(T, E) + 256 <= 64 * 1024;   // + static LDS
 }
 
+// Routing in the same launch as layout and packing: small batches of routed tokens.
+inline bool lp_route_fits(int32_t T, int32_t E, int32_t k)
+{
+    return T >= 1 && T <= kLpRouteTokens && k <= 16 && E <= 256 &&
+           lp_lds_bytes(T, E) + (size_t)T * k * sizeof(int32_t) + 256 <= 64 * 1024;
+}
+
+// Layout and packing in one launch; with `logits` non-null also the routing (lp_route_fits), whose
+// ids and weights go to topk_idx / topk_w.
 void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32_t E,
                         int32_t k, const int32_t* topk_idx, const moe_dtype_t* payload_dtype,
                         const moe_dispatch_out_t* out, const CountOutputs& co, hipStream_t stream,
-                        const EpSend* ep = nullptr)
+                        const EpSend* ep = nullptr, const float* logits = nullptr,
+                        float* topk_w = nullptr)
 {
     const bool layout_only = payload_dtype == nullptr;
     const bool fp8 = !layout_only && *payload_dtype == MOE_FP8_E4M3;
@@ -2014,17 +2049,45 @@ void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H
     lp.ep_sources = ep ? ep->sources : 1;
     lp.ep_cap = ep ? ep->cap : 0;
     lp.ep_L = ep ? ep->L : 0;
+    lp.logits = logits;
+    lp.route_idx = const_cast<int32_t*>(topk_idx);
+    lp.route_w = topk_w;
     const int64_t groups = ceil_div((int64_t)T * lp.pieces, kLpWaves);
     const dim3 grid((unsigned)(groups < kLpMaxGroups ? groups : kLpMaxGroups));
+    if (logits != nullptr) {                             // routing here: payload modes only
+        const size_t lds = lp_lds_bytes(T, E) + (size_t)T * k * sizeof(int32_t);
+        const int p16 = (int)ceil_div(E, 16);
+#define MOE_LP_ROUTE(MODE)                                                                        \
+    do {                                                                                          \
+        if (p16 <= 1)                                                                             \
+            k_layout_pack<MODE, 1><<<grid, kLpThreads, lds, stream>>>(lp, co);                    \
+        else if (p16 <= 2)                                                                        \
+            k_layout_pack<MODE, 2><<<grid, kLpThreads, lds, stream>>>(lp, co);                    \
+        else if (p16 <= 4)                                                                        \
+            k_layout_pack<MODE, 4><<<grid, kLpThreads, lds, stream>>>(lp, co);                    \
+        else if (p16 <= 8)                                                                        \
+            k_layout_pack<MODE, 8><<<grid, kLpThreads, lds, stream>>>(lp, co);                    \
+        else                                                                                      \
+            k_layout_pack<MODE, 16><<<grid, kLpThreads, lds, stream>>>(lp, co);                   \
+    } while (0)
+        if (!fp8)
+            MOE_LP_ROUTE(LP_COPY);
+        else if (x_dtype == MOE_F32)
+            MOE_LP_ROUTE(LP_FP8_F32);
+        else
+            MOE_LP_ROUTE(LP_FP8_BF16);
+#undef MOE_LP_ROUTE
+        return;
+    }
     const size_t lds = lp_lds_bytes(T, E);
     if (layout_only)
-        k_layout_pack<LP_LAYOUT><<<grid, kLpThreads, lds, stream>>>(lp, co);
+        k_layout_pack<LP_LAYOUT, 0><<<grid, kLpThreads, lds, stream>>>(lp, co);
     else if (!fp8)
-        k_layout_pack<LP_COPY><<<grid, kLpThreads, lds, stream>>>(lp, co);
+        k_layout_pack<LP_COPY, 0><<<grid, kLpThreads, lds, stream>>>(lp, co);
     else if (x_dtype == MOE_F32)
-        k_layout_pack<LP_FP8_F32><<<grid, kLpThreads, lds, stream>>>(lp, co);
+        k_layout_pack<LP_FP8_F32, 0><<<grid, kLpThreads, lds, stream>>>(lp, co);
     else
-        k_layout_pack<LP_FP8_BF16><<<grid, kLpThreads, lds, stream>>>(lp, co);
+        k_layout_pack<LP_FP8_BF16, 0><<<grid, kLpThreads, lds, stream>>>(lp, co);
 }
 
 template <typename YT, typename OT>
@@ -2181,6 +2244,12 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)T * k;
+    if (lp_route_fits(T, E, k)) {
+        // the smallest batches: routing, layout and packing in one launch
+        launch_layout_pack(x, x_dtype, T, H, E, k, topk_idx, &payload_dtype, out,
+                           count_outputs(out, n_ranks), stream, nullptr, logits, topk_w);
+        return launch_status();
+    }
     if (lp_fits(T, E)) {
         // small batches: routing, then layout and packing in one launch
         launch_route(logits, T, E, k, topk_idx, topk_w, stream);

@@ -171,6 +171,11 @@ EDGE = [
     (449, 512, 1024, 2, 4, "bf16", "bf16"),     # one token more: the multi-launch layout
     (512, 1536, 256, 8, 32, "bf16", "bf16"),    # most tokens the one-launch layout takes
     (513, 512, 64, 2, 4, "bf16", "bf16"),       # one token more: the multi-launch layout
+    # routing in the same launch as layout and packing (up to 32 tokens, k <= 16, E <= 256)
+    (32, 256, 256, 16, 16, "bf16", "bf16"),     # at every limit
+    (33, 256, 256, 16, 16, "f32", "fp8_e4m3"),  # one token more: a separate routing launch
+    (8, 128, 264, 4, 4, "bf16", "fp8_e4m3"),    # E past the limit
+    (8, 128, 64, 17, 4, "bf16", "bf16"),        # k past the limit
 ]
 
 

@@ -1227,18 +1227,20 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
             id = lp.topk_idx[t * k + lane];
     }
 
-    // routing (RP > 0, at most kLpRouteTokens tokens and k <= 16): every workgroup routes the whole
-    // batch, 16 lanes a token, into LDS; workgroup 0 also writes the ids and weights
+    // routing (RP > 0, k <= 16): every workgroup routes the whole batch into LDS, 16 lanes a
+    // token, kLpThreads / 16 tokens a pass; workgroup 0 also writes the ids and weights
     if constexpr (RP > 0) {
-        const int q = tid >> 4;                          // token, 0 .. kLpThreads / 16 - 1
-        const bool valid = q < lp.T;
-        float lg[RP];
-        load_logits16<RP>(lp.logits + (int64_t)(valid ? q : 0) * E, valid ? E : 0, lg);
-        const bool out = blockIdx.x == 0 && valid;
-        const int my = route_row16<RP>(lg, E, k, valid, out ? lp.route_idx + q * k : nullptr,
-                                       out ? lp.route_w + q * k : nullptr);
-        if (valid && (tid & 15) < k)
-            ids[q * k + (tid & 15)] = my;
+        for (int q0 = 0; q0 < lp.T; q0 += kLpThreads / 16) {     // uniform across the workgroup
+            const int q = q0 + (tid >> 4);
+            const bool valid = q < lp.T;
+            float lg[RP];
+            load_logits16<RP>(lp.logits + (int64_t)(valid ? q : 0) * E, valid ? E : 0, lg);
+            const bool out = blockIdx.x == 0 && valid;
+            const int my = route_row16<RP>(lg, E, k, valid, out ? lp.route_idx + q * k : nullptr,
+                                           out ? lp.route_w + q * k : nullptr);
+            if (valid && (tid & 15) < k)
+                ids[q * k + (tid & 15)] = my;
+        }
         __syncthreads();
         if (u < units && lane < k)
             id = ids[t * k + lane];

@@ -16,8 +16,8 @@
 //                    (token, slot) from one LDS bit mask per expert;
 //   k_layout_hist    for caller-given expert ids: per block of items, stable in-block ranks from
 //                    per-wavefront LDS bit masks, and the block's expert histogram;
-//   k_expert_scan    one wavefront per expert scans its blocks' counts into per-block prefixes
-//                    and the expert's total (many workgroups);
+//   k_expert_scan    four experts per workgroup: coalesced gathers of the blocks' counts, then a
+//                    wavefront per expert scans them into per-block prefixes and the total;
 //   k_layout_rows    every workgroup scans the expert totals into offsets in LDS, then writes
 //                    token_row / row_token; workgroup 0 writes the counts and offsets;
 //   k_pack_rows      one wavefront per (token, slot, 1 KB piece of the row): a 16-byte load of
@@ -29,7 +29,7 @@
 //                    and packs its pieces, so layout and packing take one launch; up to 32 routed
 //                    tokens every workgroup also routes the batch itself, so dispatch is one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
-//                    fp32 fused multiply-adds, one 16-byte store per 8 outputs;
+//                    fp32 fused multiply-adds, one 16-byte store (cache policy sc1) per 8 outputs;
 //   k_ep_recv_plan   expert-parallel receive: every workgroup scans a rank's per-(source, expert)
 //                    region counts into the grouped layout and finds the region row of its share
 //                    of the grouped rows;
@@ -51,21 +51,56 @@ constexpr int kGroupThreads = 1024;      // 16-wavefront workgroups (route-layou
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kRouteTokens = kGroupWaves;   // route-layout workgroup, k > 16: a token a wave
 constexpr int kRouteTokens16 = kThreads / 16;   // route-layout workgroup, k <= 16: 16 lanes each
-constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan wavefront takes (16 a lane)
+constexpr int kMaxScanBlocks = 64 * 16;  // histogram blocks one scan takes (64 threads of 16 each)
+constexpr int kScanExperts = kThreads / 64;   // experts per scan workgroup (a wavefront each)
 constexpr int kPackWaves = 16;           // wavefronts per pack / copy workgroup
 constexpr int kPackWavesWindows = 8;     //   (8 for the window-ordered pack)
 constexpr int kPackSplitPieces = 12;     // window order: rows of fewer 1 KB pieces take 2 a wave
 constexpr int kMaxEpSegments = 4096;     // expert-parallel receive: sources x local experts
 constexpr int kCombineWaves = 1;         // wavefronts per combine workgroup
-constexpr int kXcds = 8;
+constexpr int kXcds = 8;                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
 constexpr int kLpTokens = 512;           // layout folded into packing: at most this many tokens
 constexpr int kLpThreads = 512;          //   (8 wavefronts a workgroup, two experts a thread)
 constexpr int kLpWaves = kLpThreads / 64;
 constexpr int kLpMaxGroups = 1024;       //   (grid-stride beyond this many workgroups)
-constexpr int kLpRouteTokens = kLpThreads / 16;   // routing in the same launch: at most 32 tokens                 // workgroup b runs on XCD b % 8 (round-robin dispatch)
+constexpr int kLpRouteTokens = kLpThreads / 16;   // routing in the same launch: at most 32 tokens
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------ policy stores --
+// Cache-policy bits of a gfx950 buffer store (its sc0 = 1, nt = 2 and sc1 = 16 fields). Measured
+// on MI355X against non-temporal stores: combine's output (59 MB, written between 470 MB of
+// non-temporal reads) goes out faster with sc1 alone. The packed rows do not: with nt and sc1
+// the window-ordered pack of a prefill batch was about 20 us slower, so they keep nt.
+enum StorePolicy { kStoreNt = 2, kStoreSc1 = 16, kStoreNtSc1 = 18 };
+
+// Word 3 of a raw buffer resource on gfx9-family GPUs: 32-bit data format, no swizzle, no index
+// stride (the instruction's size decides how much it moves).
+constexpr int kBufferWord3 = 0x00020000;
+
+// A 16-byte store of v at byte offset `off` of the range [base, base + bytes), with the cache
+// policy POLICY. base must be the same in every lane of the wavefront (it becomes the scalar
+// buffer resource); a store at or beyond `bytes` is dropped by the hardware's range check.
+template <int POLICY>
+__device__ __forceinline__ void store16_policy(void* base, uint32_t bytes, uint32_t off, u32x4 v)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kBufferWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, POLICY);
+}
+
+// A pointer made wavefront-uniform (its value in the first active lane), for values that are the
+// same in every lane by construction but that the compiler cannot prove uniform.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return (P*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 
 // ---------------------------------------------------------------------------- number formats --
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -590,40 +625,53 @@ __global__ __launch_bounds__(kThreads) void k_layout_hist(const int32_t* __restr
         hist[(int64_t)blockIdx.x * E + e] = run[e];
 }
 
-// Scan of the block histograms, one wavefront per expert e (16 per workgroup, many workgroups).
-// Lane l gathers the counts of e in blocks l*S .. l*S+S-1 (the 16 wavefronts of a workgroup read
-// neighbouring words of the same block rows); a wave scan of the lane sums gives
-// prefix[e * nblk + b] = rows of e in blocks before b, and e's total goes to totals[e].
+// Scan of the block histograms (stored block-major, hist[b * E + e]). A workgroup takes
+// kScanExperts neighbouring experts: thread (q, u) = (tid / kScanExperts, tid % kScanExperts)
+// gathers the counts of expert e = first + u in blocks q*S .. q*S+S-1, so one load instruction of a
+// wavefront reads 16 short runs of kScanExperts words instead of 64 scattered words. Wavefront u
+// then scans the 64 per-thread sums of expert u in LDS, and every thread writes its S exclusive
+// prefixes: prefix[e * nblk + b] = rows of e in blocks before b; e's total goes to totals[e].
 // Requires nblk <= 64 * S (nblk = 0 gives zero totals).
 template <int S>
-__global__ __launch_bounds__(kGroupThreads) void k_expert_scan(const uint32_t* __restrict__ hist,
-                                                               int32_t E, int32_t nblk,
-                                                               uint32_t* __restrict__ prefix,
-                                                               uint32_t* __restrict__ totals)
+__global__ __launch_bounds__(kThreads) void k_expert_scan(const uint32_t* __restrict__ hist,
+                                                          int32_t E, int32_t nblk,
+                                                          uint32_t* __restrict__ prefix,
+                                                          uint32_t* __restrict__ totals)
 {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * kGroupWaves + (threadIdx.x >> 6);
-    if (e >= E)
-        return;                                          // uniform per wavefront
+    static_assert(kThreads == 64 * kScanExperts, "one scanning wavefront per expert");
+    __shared__ uint32_t part[kScanExperts * 64];
+    const int u = threadIdx.x % kScanExperts;
+    const int q = threadIdx.x / kScanExperts;
+    const int e = blockIdx.x * kScanExperts + u;
+    const bool valid = e < E;                            // no early return: barriers follow
     uint32_t c[S];
     uint32_t sum = 0u;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const int b = lane * S + s;
-        c[s] = b < nblk ? hist[(int64_t)b * E + e] : 0u;
+        const int b = q * S + s;
+        c[s] = (valid && b < nblk) ? hist[(int64_t)b * E + e] : 0u;
         sum += c[s];
     }
-    const uint32_t incl = wave_inclusive_scan_u32(sum);
-    uint32_t run = incl - sum;
+    part[u * 64 + q] = sum;
+    __syncthreads();
+    {
+        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const uint32_t v = part[w * 64 + lane];
+        const uint32_t incl = wave_inclusive_scan_u32(v);
+        part[w * 64 + lane] = incl - v;
+        const int ew = blockIdx.x * kScanExperts + w;
+        if (lane == 63 && ew < E)
+            totals[ew] = incl;
+    }
+    __syncthreads();
+    uint32_t run = part[u * 64 + q];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const int b = lane * S + s;
-        if (b < nblk)
+        const int b = q * S + s;
+        if (valid && b < nblk)
             prefix[(int64_t)e * nblk + b] = run;
         run += c[s];
     }
-    if (lane == 63)
-        totals[e] = incl;
 }
 
 // The count outputs of dispatch: expert and rank counts and offsets (offsets end with the row
@@ -1421,6 +1469,19 @@ struct Store8<uint16_t> {
         o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p));
     }
+    // The 8 outputs at element `off` of the wavefront-uniform row `row` of `n` elements, stored
+    // with the cache policy POLICY.
+    template <int POLICY>
+    static __device__ __forceinline__ void run_policy(uint16_t* row, uint32_t n, uint32_t off,
+                                                      const float (&acc)[8])
+    {
+        u32x4 o;
+        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+        store16_policy<POLICY>(row, n * 2u, off * 2u, o);
+    }
 };
 
 template <>
@@ -1434,6 +1495,18 @@ struct Store8<float> {
         b.z = __float_as_uint(acc[6]); b.w = __float_as_uint(acc[7]);
         __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(p));
         __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(p) + 1);
+    }
+    template <int POLICY>
+    static __device__ __forceinline__ void run_policy(float* row, uint32_t n, uint32_t off,
+                                                      const float (&acc)[8])
+    {
+        u32x4 a, b;
+        a.x = __float_as_uint(acc[0]); a.y = __float_as_uint(acc[1]);
+        a.z = __float_as_uint(acc[2]); a.w = __float_as_uint(acc[3]);
+        b.x = __float_as_uint(acc[4]); b.y = __float_as_uint(acc[5]);
+        b.z = __float_as_uint(acc[6]); b.w = __float_as_uint(acc[7]);
+        store16_policy<POLICY>(row, n * 4u, off * 4u, a);
+        store16_policy<POLICY>(row, n * 4u, off * 4u + 16u, b);
     }
 };
 
@@ -1487,7 +1560,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_combine(
             v.fma_into(topk_w[t * k + j], acc);
         }
     }
-    Store8<OT>::run(out + t * H + off, acc);
+    Store8<OT>::template run_policy<kStoreSc1>(uniform_ptr(out + t * H), (uint32_t)H,
+                                               (uint32_t)off, acc);
 }
 
 
@@ -1790,6 +1864,8 @@ moe_status_t check_pack_args(const void* x, moe_dtype_t x_dtype, int32_t T, int3
     }
     if (((int64_t)H * (int64_t)dtype_size(x_dtype)) % 16 != 0)
         return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)H * (int64_t)dtype_size(x_dtype) > INT32_MAX)
+        return MOE_ERR_UNSUPPORTED;                      // row stores address 32-bit ranges
     if (!aligned(x, 16) || !aligned(recv, 16))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -1908,11 +1984,10 @@ void launch_scan_rows(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E,
                       const EpSend* ep, const Workspace& ws, const LayoutPlan& plan,
                       const WindowPlan& wp, hipStream_t stream)
 {
-    const dim3 grid((unsigned)ceil_div(E, kGroupWaves));
+    const dim3 grid((unsigned)ceil_div(E, kScanExperts));
     const int64_t s = ceil_div(plan.nblk, 64);
 #define MOE_SCAN(SS)                                                                              \
-    k_expert_scan<SS><<<grid, kGroupThreads, 0, stream>>>(ws.hist, E, plan.nblk, ws.prefix,      \
-                                                          ws.totals)
+    k_expert_scan<SS><<<grid, kThreads, 0, stream>>>(ws.hist, E, plan.nblk, ws.prefix, ws.totals)
     if (s <= 1)
         MOE_SCAN(1);
     else if (s <= 2)
@@ -2304,8 +2379,8 @@ static moe_status_t combine_checked(const void* y, moe_dtype_t y_dtype, int32_t 
         return MOE_ERR_INVALID;
     if (!is_wide(y_dtype) || !is_wide(out_dtype))
         return MOE_ERR_UNSUPPORTED;
-    if (H % 8 != 0)
-        return MOE_ERR_UNSUPPORTED;
+    if (H % 8 != 0 || (int64_t)H * (int64_t)dtype_size(out_dtype) > INT32_MAX)
+        return MOE_ERR_UNSUPPORTED;                      // output stores address 32-bit ranges
     if (T > 0 && (!y || !token_row || !topk_w || !out))
         return MOE_ERR_INVALID;
     if (!aligned(y, 16) || !aligned(out, 16))

@@ -9,9 +9,13 @@ bf16 payload and output). The expert outputs combine reads are emulated once bef
 
 Prints ONE JSON line: value = algorithmic HBM bytes of a step / step time (GB/s), ms_per_step =
 µs per layer / 1000, per-call times from HIP events on the launch stream, the roofline of the
-dominant kernel, and the CPU oracle timed on the host. Two more timed loops run the same step as
-route -> moe_dispatch -> combine and as route -> moe_dispatch_layout -> moe_dispatch_pack ->
-combine, so the packing kernel gets its own HIP-event timing.
+dominant kernel (combine), and the CPU oracle timed on the host. Two more timed loops run the same
+step as route -> moe_dispatch -> combine and as route -> moe_dispatch_layout ->
+moe_dispatch_pack -> combine, so the token-order packing kernel gets its own HIP-event timing.
+
+The steps rotate over 8 buffer sets by default, so that every set's activations and logits have
+left the 256 MB Infinity Cache when the set comes round again: the numbers are cold. A warm step
+(one set) is reported beside them.
 """
 from __future__ import annotations
 
@@ -43,8 +47,11 @@ def parse_args():
     p.add_argument("--settle-seconds", type=float, default=0.3,
                    help="before the warmup steps, run the plain copy kernel this long so the GPU "
                         "reaches its steady clocks (0 disables it)")
-    p.add_argument("--sets", type=int, default=2,
-                   help="buffer sets used in rotation (each set is about 1 GB at prefill)")
+    p.add_argument("--sets", type=int, default=8,
+                   help="buffer sets used in rotation (each set is about 1 GB at prefill). With "
+                        "2 sets the activations and logits of a set (65 MB at prefill) are still "
+                        "in the 256 MB Infinity Cache when the set comes round again; from 6 sets "
+                        "on they are not (measured: the same step time at 6 and 8 sets)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="host time budget of the CPU-oracle baseline (0 disables it)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -277,17 +284,18 @@ def timed(torch, sets, phases, K, per_call_events):
 HEADLINE = ("route_dispatch", "combine")
 
 
-def other_workloads(torch, moe, dev, names, K):
-    """The headline step on the smaller workloads (latency-bound ones are reported in us)."""
+def other_workloads(torch, moe, dev, names, K, n_sets):
+    """The headline step on the smaller workloads (latency-bound ones are reported in us), over
+    n_sets buffer sets in rotation."""
     from combine_moe_route_03_amd.workloads import WORKLOADS, make_inputs
     res = {}
     for name in names:
         w = WORKLOADS[name]
         inp = make_inputs(w)
-        sets = [make_set(w, inp, dev, moe, torch) for _ in range(2)]
+        sets = [make_set(w, inp, dev, moe, torch) for _ in range(n_sets)]
         for i in range(10):
             for ph in HEADLINE:
-                sets[i % 2][ph]()
+                sets[i % n_sets][ph]()
         ms, _, _ = timed(torch, sets, HEADLINE, K, False)
         _, per, steps = timed(torch, sets, HEADLINE, K, True)
         alg = sum(algorithmic_bytes(w).values())
@@ -496,15 +504,15 @@ def main():
     alg = algorithmic_bytes(w)
     alg_total = sum(alg.values())
     value = alg_total / (ms_per_step * 1e-3) / 1e9
-    # The dominant kernel: packing (its token-order form, launched alone through moe_dispatch_pack;
-    # the dispatch entry points use the window-ordered form, seen in the kernel trace) or combine,
-    # each timed over K back-to-back launches of that kernel alone (two events around the loop),
-    # which is what a kernel trace averages.
+    # The dominant kernel of the step is combine: the step's other long kernel, the window-ordered
+    # pack inside moe_route_dispatch, finds x already read ahead by the layout launches and runs
+    # shorter (83-84 us against 86-88 us at prefill in the cold kernel trace). Combine is timed over
+    # K back-to-back launches of itself (two events around the loop), which is what a kernel trace
+    # averages. The token-order pack of moe_dispatch_pack, which is not part of the step and reads
+    # x as it packs, is timed the same way for context.
     kernel_us = {ph: timed(torch, sets, (ph,), K, False)[0] * 1e3 for ph in ("pack", "combine")}
-    dominant = max(kernel_us, key=lambda ph: kernel_us[ph])
-    # the pack timed alone is the token-order form: k_pack_rows<0, 1> (order 0, one piece a wave)
-    pattern = {"pack": r"k_pack_rows<0, 1>|k_pack_rows_fp8<.*>",
-               "combine": r"k_combine<.*>"}[dominant]
+    dominant = "combine"
+    pattern = r"k_combine<.*>"
     prof_name, traffic = hbm_traffic(pattern)
     kernel_name = prof_name or {"pack": "k_pack_rows" if w.payload != "fp8_e4m3"
                                 else "k_pack_rows_fp8", "combine": "k_combine"}[dominant]
@@ -525,7 +533,7 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] other workloads", file=sys.stderr, flush=True)
         others = other_workloads(torch, moe, dev, ("tiny", "decode", "decode_fp8", "skewed"),
-                                 100)
+                                 100, max(1, args.sets))
         print("[bench] " + "; ".join(f"{n} {r['us_per_step']} us" for n, r in others.items()),
               file=sys.stderr, flush=True)
         ep = ep_emulation(torch, moe, dev, 20)
@@ -555,7 +563,8 @@ def main():
         "config": {"workload": f"{w.name}: {w.T} tokens, hidden {w.H} {w.x_dtype}, {w.E} experts "
                                f"top-{w.k}, {w.N} ranks, {w.payload} payload, {w.out_dtype} out",
                    "tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k, "ranks": w.N,
-                   "payload": w.payload, "parallelism": "single GPU"},
+                   "payload": w.payload, "parallelism": "single GPU",
+                   "buffer_sets": max(1, args.sets)},
         "us_per_layer": round(ms_per_step * 1e3, 2),
         "us_route_dispatch_plus_combine": round(phase_us["route_dispatch"] +
                                                 phase_us["combine"], 2),
@@ -575,7 +584,8 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg[dominant],
                      "avg_launch_us": round(kernel_us[dominant], 2)},
-        "kernel_alone_us": {ph: round(v, 2) for ph, v in kernel_us.items()},
+        "kernel_alone_us": {"combine": round(kernel_us["combine"], 2),
+                            "token_order_pack": round(kernel_us["pack"], 2)},
         "copy_ceiling_GBps": round(ceiling["GBps"], 1),
         "other_workloads": others,
         "ep_emulation": ep,

@@ -161,6 +161,11 @@ EDGE = [
     (32, 512, 256, 8, 32, "bf16", "fp8_e4m3"),  # one mask word a token block
     (16384, 128, 64, 2, 4, "bf16", "bf16"),     # most tokens the fused route-layout takes
     (16401, 128, 64, 2, 4, "f32", "f32"),       # one token more: separate route + histogram
+    # the multi-launch layout reads x ahead in its launches (thirds, or halves when routing takes a
+    # wavefront a token); every part must stay inside x
+    (700, 2056, 64, 4, 8, "bf16", "bf16"),      # a wavefront a token (T < 1024), ragged row tail
+    (1100, 256, 384, 20, 48, "f32", "f32"),     # k > 16 past 1024 tokens
+    (1024, 1024, 256, 8, 32, "bf16", "fp8_e4m3"),   # fp8 packing after the multi-launch layout
     # layout folded into packing (up to 512 tokens through moe_route_dispatch)
     (100, 4104, 64, 4, 8, "bf16", "bf16"),      # ragged 16-byte tail, tokens across 4 mask words
     (200, 256, 384, 32, 48, "f32", "f32"),      # k > 16 (a wavefront a token in routing)

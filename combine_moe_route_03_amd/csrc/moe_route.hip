@@ -29,7 +29,7 @@
 //                    and packs its pieces, so layout and packing take one launch; up to 32 routed
 //                    tokens every workgroup also routes the batch itself, so dispatch is one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
-//                    fp32 fused multiply-adds, one 16-byte store (cache policy sc1) per 8 outputs;
+//                    fp32 fused multiply-adds, one 16-byte non-temporal store per 8 outputs;
 //   k_ep_recv_plan   expert-parallel receive: every workgroup scans a rank's per-(source, expert)
 //                    region counts into the grouped layout and finds the region row of its share
 //                    of the grouped rows;
@@ -67,40 +67,6 @@ constexpr int kLpRouteTokens = kLpThreads / 16;   // routing in the same launch:
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-// ------------------------------------------------------------------------ policy stores --
-// Cache-policy bits of a gfx950 buffer store (its sc0 = 1, nt = 2 and sc1 = 16 fields). Measured
-// on MI355X against non-temporal stores: combine's output (59 MB, written between 470 MB of
-// non-temporal reads) goes out faster with sc1 alone. The packed rows do not: with nt and sc1
-// the window-ordered pack of a prefill batch was about 20 us slower, so they keep nt.
-enum StorePolicy { kStoreNt = 2, kStoreSc1 = 16, kStoreNtSc1 = 18 };
-
-// Word 3 of a raw buffer resource on gfx9-family GPUs: 32-bit data format, no swizzle, no index
-// stride (the instruction's size decides how much it moves).
-constexpr int kBufferWord3 = 0x00020000;
-
-// A 16-byte store of v at byte offset `off` of the range [base, base + bytes), with the cache
-// policy POLICY. base must be the same in every lane of the wavefront (it becomes the scalar
-// buffer resource); a store at or beyond `bytes` is dropped by the hardware's range check.
-template <int POLICY>
-__device__ __forceinline__ void store16_policy(void* base, uint32_t bytes, uint32_t off, u32x4 v)
-{
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kBufferWord3);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, POLICY);
-}
-
-// A pointer made wavefront-uniform (its value in the first active lane), for values that are the
-// same in every lane by construction but that the compiler cannot prove uniform.
-template <typename P>
-__device__ __forceinline__ P* uniform_ptr(P* p)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    return (P*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
 
 // ---------------------------------------------------------------------------- number formats --
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -1532,19 +1498,6 @@ struct Store8<uint16_t> {
         o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p));
     }
-    // The 8 outputs at element `off` of the wavefront-uniform row `row` of `n` elements, stored
-    // with the cache policy POLICY.
-    template <int POLICY>
-    static __device__ __forceinline__ void run_policy(uint16_t* row, uint32_t n, uint32_t off,
-                                                      const float (&acc)[8])
-    {
-        u32x4 o;
-        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-        store16_policy<POLICY>(row, n * 2u, off * 2u, o);
-    }
 };
 
 template <>
@@ -1558,18 +1511,6 @@ struct Store8<float> {
         b.z = __float_as_uint(acc[6]); b.w = __float_as_uint(acc[7]);
         __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(p));
         __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(p) + 1);
-    }
-    template <int POLICY>
-    static __device__ __forceinline__ void run_policy(float* row, uint32_t n, uint32_t off,
-                                                      const float (&acc)[8])
-    {
-        u32x4 a, b;
-        a.x = __float_as_uint(acc[0]); a.y = __float_as_uint(acc[1]);
-        a.z = __float_as_uint(acc[2]); a.w = __float_as_uint(acc[3]);
-        b.x = __float_as_uint(acc[4]); b.y = __float_as_uint(acc[5]);
-        b.z = __float_as_uint(acc[6]); b.w = __float_as_uint(acc[7]);
-        store16_policy<POLICY>(row, n * 4u, off * 4u, a);
-        store16_policy<POLICY>(row, n * 4u, off * 4u + 16u, b);
     }
 };
 
@@ -1623,8 +1564,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_combine(
             v.fma_into(topk_w[t * k + j], acc);
         }
     }
-    Store8<OT>::template run_policy<kStoreSc1>(uniform_ptr(out + t * H), (uint32_t)H,
-                                               (uint32_t)off, acc);
+    Store8<OT>::run(out + t * H + off, acc);
 }
 
 
@@ -1930,8 +1870,6 @@ moe_status_t check_pack_args(const void* x, moe_dtype_t x_dtype, int32_t T, int3
     }
     if (((int64_t)H * (int64_t)dtype_size(x_dtype)) % 16 != 0)
         return MOE_ERR_UNSUPPORTED;
-    if ((int64_t)H * (int64_t)dtype_size(x_dtype) > INT32_MAX)
-        return MOE_ERR_UNSUPPORTED;                      // row stores address 32-bit ranges
     if (!aligned(x, 16) || !aligned(recv, 16))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -2496,8 +2434,8 @@ static moe_status_t combine_checked(const void* y, moe_dtype_t y_dtype, int32_t 
         return MOE_ERR_INVALID;
     if (!is_wide(y_dtype) || !is_wide(out_dtype))
         return MOE_ERR_UNSUPPORTED;
-    if (H % 8 != 0 || (int64_t)H * (int64_t)dtype_size(out_dtype) > INT32_MAX)
-        return MOE_ERR_UNSUPPORTED;                      // output stores address 32-bit ranges
+    if (H % 8 != 0)
+        return MOE_ERR_UNSUPPORTED;
     if (T > 0 && (!y || !token_row || !topk_w || !out))
         return MOE_ERR_INVALID;
     if (!aligned(y, 16) || !aligned(out, 16))

@@ -121,8 +121,7 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, 
  *     token and block b of 128 elements, amax = max |x|, s = amax / 448 in fp32 (1 when amax = 0),
  *     code = e4m3(x / s) rounded to nearest even and saturated to +-448;
  *     recv [R, H] uint8 codes, recv_scales [R, H/128] fp32 s. Requires H % 128 == 0.
- *   recv 16-byte aligned, recv_scales 4-byte aligned. An x row of more than 2^31 - 1 bytes
- *   returns MOE_ERR_UNSUPPORTED.
+ *   recv 16-byte aligned, recv_scales 4-byte aligned.
  */
 moe_status_t moe_dispatch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H,
                                int32_t k, const int32_t* token_row, moe_dtype_t payload_dtype,
@@ -161,8 +160,7 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
  *   out       [T, H] out_dtype MOE_F32 or MOE_BF16, 16-byte aligned:
  *             out[t, h] = sum_{j<k} w[t, j] * y[token_row[t*k+j], h], accumulated in fp32 in
  *             slot order (fused multiply-add), rounded to nearest even for bf16.
- * Requires H % 8 == 0 and an output row of at most 2^31 - 1 bytes (else MOE_ERR_UNSUPPORTED).
- * T = 0 enqueues nothing.
+ * Requires H % 8 == 0. T = 0 enqueues nothing.
  */
 moe_status_t moe_combine(const void* y, moe_dtype_t y_dtype, int32_t T, int32_t H, int32_t k,
                          const int32_t* token_row, const float* topk_w, void* out,

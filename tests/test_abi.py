@@ -131,16 +131,6 @@ def test_pack_validation():
     assert f(None, BF16, 0, 256, 2, None, BF16, None, None, S0) == moe.MOE_OK            # T = 0
 
 
-def test_pack_rejects_rows_past_31_bit_byte_offsets():
-    # row stores address one x row's bytes with 32-bit offsets: rows of 2^31 bytes are refused
-    f = moe.load().moe_dispatch_pack
-    F32, BF16, FP8 = moe.MOE_F32, moe.MOE_BF16, moe.MOE_FP8_E4M3
-    U = moe.MOE_ERR_UNSUPPORTED
-    assert f(A16, F32, 1, 1 << 29, 1, A16, F32, A16b, None, S0) == U       # 2^29 fp32 = 2^31 B
-    assert f(A16, BF16, 1, 1 << 30, 1, A16, BF16, A16b, None, S0) == U     # 2^30 bf16 = 2^31 B
-    assert f(A16, F32, 1, 1 << 29, 1, A16, FP8, A16b, A16, S0) == U        # x row counts
-
-
 def test_dispatch_validation_checks_both_halves():
     f = moe.load().moe_dispatch
     o = _out_struct()
@@ -276,17 +266,6 @@ def test_combine_validation():
     assert f(A16, BF16, 4, 256, 2, A16, None, A16b, BF16, S0) == moe.MOE_ERR_INVALID
     assert f(A16, BF16, 4, 256, 0, A16, A16, A16b, BF16, S0) == moe.MOE_ERR_INVALID
     assert f(None, BF16, 0, 256, 2, None, None, None, BF16, S0) == moe.MOE_OK
-
-
-def test_combine_rejects_output_rows_past_31_bit_byte_offsets():
-    # the output row is stored with 32-bit byte offsets: rows of 2^31 bytes are refused, before
-    # any launch (and also for T = 0)
-    f = moe.load().moe_combine
-    F32, BF16 = moe.MOE_F32, moe.MOE_BF16
-    U = moe.MOE_ERR_UNSUPPORTED
-    assert f(A16, BF16, 1, 1 << 29, 1, A16, A16, A16b, F32, S0) == U       # 2^29 fp32 outputs
-    assert f(A16, F32, 1, 1 << 30, 1, A16, A16, A16b, BF16, S0) == U       # 2^30 bf16 outputs
-    assert f(None, BF16, 0, 1 << 29, 1, None, None, None, F32, S0) == U
 
 
 def test_check_topk_validation():

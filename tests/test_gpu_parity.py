@@ -395,3 +395,34 @@ def test_layout_only_and_pack_only_match_dispatch():
     torch.cuda.synchronize()
     _check_layout(buf, d)
     _check_payload(buf, d, w.payload)
+
+
+def test_one_dirty_workspace_serves_shapes_of_every_path():
+    """The workspace needs no initialisation and may be larger than asked for: one buffer, filled
+    with 0xFF bytes, serves in turn the multi-launch paths (routed: thirds of x read ahead; wide
+    routing: halves; caller-given ids) and the one-launch paths, each output equal to the oracle's."""
+    shapes = [(4096, 1024, 384, 8, 48, "bf16"),    # 16 lanes a token, read-ahead in thirds
+              (700, 2048, 64, 4, 8, "bf16"),       # a wavefront a token: read-ahead in halves
+              (1100, 512, 384, 20, 48, "f32"),     # k > 16 past 1024 tokens
+              (300, 1024, 64, 4, 8, "bf16"),       # one launch for layout and packing
+              (16, 256, 8, 2, 2, "f32")]           # routing in that launch too
+    need = max(moe.moe_dispatch_workspace_bytes(T, E, k) for T, _, E, k, _, _ in shapes)
+    ws = torch.full((need + 4096,), 0xFF, dtype=torch.uint8, device="cuda")
+    for T, H, E, k, N, dt in shapes:
+        _announce(f"dirty workspace T={T} H={H} E={E} k={k} N={N} {dt}")
+        inp = _edge_inputs(T, H, E, k, dt, seed=T + k)
+        idx, wt = oracle.route(inp["logits"], k)
+        d = oracle.dispatch(inp["x"], dt, idx, E, N, dt)
+        buf = moe.alloc_dispatch_out(T, H, E, k, N, dt)
+        g_idx, g_w, _ = moe.moe_route_dispatch(to_dev(inp["logits"], "f32"), to_dev(inp["x"], dt),
+                                               k, N, buf, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(g_idx), idx)
+        _check_weights(to_host(g_w), wt)
+        _check_layout(buf, d)
+        _check_payload(buf, d, dt)
+        buf2 = moe.alloc_dispatch_out(T, H, E, k, N, dt)         # caller-given ids
+        moe.moe_dispatch(to_dev(inp["x"], dt), to_dev(idx, "i32"), E, N, buf2, ws)
+        torch.cuda.synchronize()
+        _check_layout(buf2, d)
+        _check_payload(buf2, d, dt)

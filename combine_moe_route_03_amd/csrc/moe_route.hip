@@ -20,9 +20,10 @@
 //                    wavefront per expert scans them into per-block prefixes and the total;
 //   k_layout_rows    every workgroup scans the expert totals into offsets in LDS, then writes
 //                    token_row / row_token; workgroup 0 writes the counts and offsets;
-//   k_pack_rows      one wavefront per (token, slot, 1 KB piece of the row): a 16-byte load of
-//                    x (from the XCD's L2 after the first of the token's wavefronts) and a
-//                    16-byte non-temporal store per lane; the pieces of a row run side by side;
+//   k_pack_rows      window order: one wavefront per (destination row, 1 KB piece), a 16-byte
+//                    load of x (from the XCD's L2 after the window's first touch) and a 16-byte
+//                    non-temporal store per lane; token order: one wavefront per (token, 1 KB
+//                    piece), one load stored to all k rows; the pieces of a row run side by side;
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
 //   k_layout_pack    batches of up to 512 tokens: every workgroup rebuilds the whole layout in
 //                    LDS from the ids (LDS counts, one block scan, token bit masks for the ranks)
@@ -978,10 +979,11 @@ __device__ __forceinline__ XcdItem xcd_item(int waves_per_group, int items_per_t
     return it;
 }
 
-// Which row a packing wavefront copies, and from which token. TOKEN_ORDER: wavefront
-// (token t, slot j, piece) with row token_row[t*k + j]; the k*pieces wavefronts of a token run on
-// one XCD (tokens x, x+8, ... on XCD x), so x's row is read from HBM once and then from that
-// L2. WINDOWS: wavefront (window w, list position q, piece) with (row, token) = list[w*rw + q];
+// Which rows a packing wavefront writes, and from which token. TOKEN_ORDER: wavefront (token t,
+// piece) loads its piece of x once and stores it to all k rows token_row[t*k + j]; the pieces
+// wavefronts of a token run on one XCD (tokens x, x+8, ... on XCD x). One load for k stores keeps
+// k times more bytes in flight per wavefront than one store per load, which is what hides x
+// coming from HBM (prefill, x cold, the pack alone: 105-108 us against 130-138 us). WINDOWS: wavefront (window w, list position q, piece) with (row, token) = list[w*rw + q];
 // the windows of XCD x are x, x+8, ..., so the window's x rows stay in one L2 while its rows go
 // out in ascending order, which keeps the writes of the whole GPU in a narrow address range.
 enum PackOrder { PACK_TOKEN_ORDER = 0, PACK_WINDOWS = 1 };
@@ -1002,12 +1004,11 @@ struct PackPlan {
     int64_t row_limit;                // rows of the destination buffer
 };
 
-// The (token, row, piece) of a wavefront: for TOKEN_ORDER the row is read by the caller after
-// the x load has been issued (row = -1 here), for WINDOWS both come from the list. token = -1:
-// nothing to copy.
+// The (token, row, piece) of a wavefront: for TOKEN_ORDER the k rows are read by the caller
+// after the x load has been issued (row = -1 here), for WINDOWS both come from the list.
+// token = -1: nothing to copy.
 struct PackItem {
     int64_t token;
-    int64_t index;       // TOKEN_ORDER: t*k + j (where token_row holds the row)
     int32_t row;
     int piece;
 };
@@ -1017,15 +1018,12 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
 {
     PackItem it;
     it.token = -1;
-    it.index = 0;
     it.row = -1;
     it.piece = 0;
     if constexpr (ORDER == PACK_TOKEN_ORDER) {
-        const XcdItem xi = xcd_item(pack_waves<ORDER>(), pp.k * pp.pieces);
+        const XcdItem xi = xcd_item(pack_waves<ORDER>(), pp.pieces);
         if (xi.token < pp.T) {
-            const int j = xi.sub / pp.pieces;
-            it.piece = xi.sub - j * pp.pieces;
-            it.index = xi.token * pp.k + j;
+            it.piece = xi.sub;
             it.token = xi.token;
         }
     } else {
@@ -1044,11 +1042,12 @@ __device__ __forceinline__ PackItem pack_item(const PackPlan& pp)
     return it;
 }
 
-// One wavefront per (row, PPW consecutive 1 KB pieces of it): lane l copies chunks
-// (piece*PPW + p)*64 + l (16 bytes each) of x's row to the destination row with non-temporal
-// stores, all loads issued before the stores; x is read with plain loads so the wavefronts that
-// copy the same token find it in L2. The pieces of a row run side by side. A row outside [0, R) is
-// skipped. PPW > 1 only in window order.
+// One wavefront per (row, PPW consecutive 1 KB pieces of it) in window order, per (token, 1 KB
+// piece) in token order: lane l copies chunks (piece*PPW + p)*64 + l (16 bytes each) of x's row
+// to the destination row (to each of the token's k rows in token order) with non-temporal stores,
+// all loads issued before the stores; x is read with plain loads so the wavefronts of a window
+// find it in L2. The pieces of a row run side by side. A row outside [0, row_limit) is skipped.
+// PPW > 1 only in window order.
 template <int ORDER, int PPW>
 __global__ __launch_bounds__(64 * pack_waves<ORDER>()) void k_pack_rows(
     const u32x4* __restrict__ x, int32_t chunks_per_row, PackPlan pp, u32x4* __restrict__ recv)
@@ -1064,13 +1063,35 @@ __global__ __launch_bounds__(64 * pack_waves<ORDER>()) void k_pack_rows(
         if (c0 + 64 * p < chunks_per_row)
             v[p] = x[it.token * chunks_per_row + c0 + 64 * p];
     }
-    const int32_t row = ORDER == PACK_TOKEN_ORDER ? pp.token_row[it.index] : it.row;
-    if (row < 0 || (int64_t)row >= pp.row_limit)
-        return;
+    if constexpr (ORDER == PACK_TOKEN_ORDER) {
+        // the token's rows, 64 slots at a time: lane j of a group reads slot j0 + j, and the
+        // wavefront stores its piece to each of them in slot order
+        const int lane = threadIdx.x & 63;
+        const int32_t* rows = pp.token_row + it.token * pp.k;
+        for (int j0 = 0; j0 < pp.k; j0 += 64) {
+            const int32_t mine = j0 + lane < pp.k ? rows[j0 + lane] : -1;
+            const int n = pp.k - j0 < 64 ? pp.k - j0 : 64;
+            for (int j = 0; j < n; ++j) {
+                const int32_t row = __builtin_amdgcn_readlane(mine, j);
+                if (row < 0 || (int64_t)row >= pp.row_limit)
+                    continue;                            // uniform per wavefront
 #pragma unroll
-    for (int p = 0; p < PPW; ++p)
-        if (c0 + 64 * p < chunks_per_row)
-            __builtin_nontemporal_store(v[p], recv + (int64_t)row * chunks_per_row + c0 + 64 * p);
+                for (int p = 0; p < PPW; ++p)
+                    if (c0 + 64 * p < chunks_per_row)
+                        __builtin_nontemporal_store(
+                            v[p], recv + (int64_t)row * chunks_per_row + c0 + 64 * p);
+            }
+        }
+    } else {
+        const int32_t row = it.row;
+        if (row < 0 || (int64_t)row >= pp.row_limit)
+            return;
+#pragma unroll
+        for (int p = 0; p < PPW; ++p)
+            if (c0 + 64 * p < chunks_per_row)
+                __builtin_nontemporal_store(v[p],
+                                            recv + (int64_t)row * chunks_per_row + c0 + 64 * p);
+    }
 }
 
 // Copies of whole rows by a row map, grid-stride over (row, 1 KB piece) by wavefronts: GATHER
@@ -2101,7 +2122,7 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
                 k_pack_rows<PACK_WINDOWS, 1><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
         } else {
             constexpr int wpg = pack_waves<PACK_TOKEN_ORDER>();
-            const dim3 grid((unsigned)xcd_blocks(T, (int64_t)k * pp.pieces, wpg));
+            const dim3 grid((unsigned)xcd_blocks(T, pp.pieces, wpg));
             k_pack_rows<PACK_TOKEN_ORDER, 1><<<grid, 64 * wpg, 0, stream>>>(xs, cpr, pp, rv);
         }
         return;

@@ -1974,16 +1974,18 @@ inline Prefetch no_prefetch()
     return pf;
 }
 
-// Part `part` of `parts` of the x prefetch: the first kPrefetchMaxBytes of x at most (the first
-// windows pack first), cut into equal ranges of 16-byte chunks, 16 chunks a thread. x null: none.
-Prefetch make_prefetch(const void* x, int64_t x_bytes, const Workspace& ws, int part, int parts)
+// Parts [part, part + n) of `parts` equal parts of the x prefetch: the first kPrefetchMaxBytes of
+// x at most (the first windows pack first), in 16-byte chunks, 16 chunks a thread. x null, or a
+// range outside [0, parts): none.
+Prefetch make_prefetch(const void* x, int64_t x_bytes, const Workspace& ws, int part, int parts,
+                       int n = 1)
 {
-    if (part < 0 || part >= parts)
+    if (part < 0 || n < 1 || part + n > parts)
         return no_prefetch();
     Prefetch pf;
     const int64_t bytes = x_bytes < kPrefetchMaxBytes ? x_bytes : kPrefetchMaxBytes;
     const int64_t all = x != nullptr && bytes > 0 ? bytes / 16 : 0;
-    const int64_t b = all * part / parts, e = all * (part + 1) / parts;
+    const int64_t b = all * part / parts, e = all * (part + n) / parts;
     pf.x = static_cast<const u32x4*>(x) + b;
     pf.chunks = e - b;
     pf.groups = (int32_t)ceil_div(pf.chunks, (int64_t)kThreads * kPrefetchChunksPerThread);
@@ -2403,27 +2405,33 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     const Workspace ws = carve_workspace(workspace, T, E, k);
     const int64_t x_bytes = (int64_t)T * H * (int64_t)dtype_size(x_dtype);
     LayoutPlan plan;
-    // x is read ahead in thirds by the counting, scan and rows launches; the wavefront-per-token
-    // routing-and-counting launch (k > 16 or small batches) carries none, so scan and rows then
-    // take halves
+    // x is read ahead by the counting, scan and rows launches, a third each by default. The
+    // 16-lane routing-and-counting launch of many experts (E >= 256: 16 or more keys a lane) runs
+    // longest and takes half, scan and rows a quarter each (prefill step 189.6 against 190.9 us;
+    // the skewed batch of 128 experts is 0.5 us slower that way, so it keeps thirds). The
+    // wavefront-per-token routing launch (k > 16 or small batches) carries none, and scan and
+    // rows take halves.
     const bool fused = T > 0 && fused_route_fits(T, k);
-    const int parts = fused && !route_rows16(T, k) ? 2 : 3;
-    const int first = parts - 2;                         // the scan's part: 1 of 3, or 0 of 2
+    const bool wide = fused && !route_rows16(T, k);
+    const bool long_route = fused && !wide && E >= 256;
+    const int parts = wide ? 2 : (long_route ? 4 : 3);
+    const int q_route = wide ? 0 : (long_route ? 2 : 1);    // parts of each launch, in order
+    const Prefetch pf_route = make_prefetch(x, x_bytes, ws, 0, parts, q_route);
+    const Prefetch pf_scan = make_prefetch(x, x_bytes, ws, q_route, parts, 1);
+    const Prefetch pf_rows = make_prefetch(x, x_bytes, ws, q_route + 1, parts, 1);
     if (fused) {
         plan = route_plan(T, k);
-        launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan,
-                            make_prefetch(x, x_bytes, ws, 0, parts), stream);
+        launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan, pf_route, stream);
     } else {
         plan = hist_plan(R);
         if (T > 0)
             launch_route(logits, T, E, k, topk_idx, topk_w, stream);
-        launch_hist(topk_idx, R, E, ws, plan, make_prefetch(x, x_bytes, ws, 0, parts), stream);
+        launch_hist(topk_idx, R, E, ws, plan, pf_route, stream);
     }
     const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
     launch_scan_rows(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
-                     count_outputs(out, n_ranks), nullptr, ws, plan, wp,
-                     make_prefetch(x, x_bytes, ws, first, parts),
-                     make_prefetch(x, x_bytes, ws, first + 1, parts), stream);
+                     count_outputs(out, n_ranks), nullptr, ws, plan, wp, pf_scan, pf_rows,
+                     stream);
     launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
                 out->recv_scales, R, stream);
     return launch_status();

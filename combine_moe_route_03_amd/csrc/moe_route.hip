@@ -1862,8 +1862,8 @@ moe_status_t check_layout_args(const int32_t* topk_idx, int32_t T, int32_t k, in
         return MOE_ERR_INVALID;
     if ((int64_t)T * k > INT32_MAX)
         return MOE_ERR_INVALID;
-    if (E > MOE_MAX_EXPERTS)
-        return MOE_ERR_UNSUPPORTED;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK)         // the one-launch layout keeps a
+        return MOE_ERR_UNSUPPORTED;                      // token's slots in one wavefront
     if (!out->expert_counts || !out->expert_offsets || !out->rank_counts || !out->rank_offsets)
         return MOE_ERR_INVALID;
     if (T > 0 && (!topk_idx || !out->token_row || !out->row_token))
@@ -2523,6 +2523,8 @@ moe_status_t moe_ep_send(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t 
         return st;
     if (T < 0 || k < 1 || (int64_t)T * k > INT32_MAX || source < 0 || source >= n_sources)
         return MOE_ERR_INVALID;
+    if (k > MOE_MAX_TOPK)
+        return MOE_ERR_UNSUPPORTED;
     if ((int64_t)cap < moe_ep_capacity(T, E, k, n_ranks))
         return MOE_ERR_INVALID;
     if (!region_counts || (T > 0 && (!topk_idx || !send_row)))

@@ -104,6 +104,8 @@ typedef struct {
  *   rank's rows are contiguous, grouped by expert, tokens ascending inside an expert. The result
  *   is deterministic (no atomics decide a position).
  *   workspace: device memory of at least moe_dispatch_workspace_bytes(T, E, k) bytes.
+ * Requires 1 <= k <= MOE_MAX_TOPK and E <= MOE_MAX_EXPERTS (else MOE_ERR_UNSUPPORTED); this limit
+ * on k also holds for moe_dispatch, moe_route_dispatch and moe_ep_send.
  * T = 0 writes zero counts and offsets.
  */
 moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
@@ -193,7 +195,8 @@ int64_t moe_ep_capacity(int32_t T, int32_t E, int32_t k, int32_t n_ranks);
  *   region (r, source) holds its rows to rank r ordered by (expert, token, slot); writes
  *   region_counts[(r*S + source)*L + l] for every r, l, and send_row[t*k + j] = the region-array row
  *   of (t, j). Uses a workspace of moe_dispatch_workspace_bytes(T, E, k) bytes.
- * Requires cap >= moe_ep_capacity(T, E, k, n_ranks) and N*S*cap < 2^31 (else MOE_ERR_INVALID).
+ * Requires cap >= moe_ep_capacity(T, E, k, n_ranks) and N*S*cap < 2^31 (else MOE_ERR_INVALID),
+ * and k <= MOE_MAX_TOPK (else MOE_ERR_UNSUPPORTED).
  */
 moe_status_t moe_ep_send(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H,
                          const int32_t* topk_idx, int32_t k, int32_t E, int32_t n_ranks,

@@ -177,6 +177,32 @@ def test_route_dispatch_validation_checks_every_part():
     assert call(ws=MIS) == moe.MOE_ERR_UNSUPPORTED
 
 
+def test_layout_calls_reject_k_beyond_max_topk():
+    """A token's slots are handled by one wavefront in the one-launch layout, so every call that
+    lays out caller-given ids rejects k > MOE_MAX_TOPK before any launch (T = 8, E = 128)."""
+    lib = moe.load()
+    BF16 = moe.MOE_BF16
+    o = _out_struct()
+    T, E, N = 8, 128, 2
+    for k in (moe.MOE_MAX_TOPK + 1, 80):
+        need = moe.moe_dispatch_workspace_bytes(T, E, k)
+        assert need > 0
+        assert lib.moe_dispatch_layout(A16, T, k, E, N, ctypes.byref(o), A16, need, S0) == \
+            moe.MOE_ERR_UNSUPPORTED
+        assert lib.moe_dispatch(A16, BF16, T, 256, A16, k, E, N, BF16, ctypes.byref(o), A16,
+                                need, S0) == moe.MOE_ERR_UNSUPPORTED
+        assert lib.moe_route_dispatch(A16, A16, BF16, T, 256, E, k, N, BF16, A16b, A16b,
+                                      ctypes.byref(o), A16, need, S0) == moe.MOE_ERR_UNSUPPORTED
+        cap = lib.moe_ep_capacity(T, E, k, N)
+        assert lib.moe_ep_send(A16, BF16, T, 256, A16, k, E, N, 0, 1, cap, A16b, A16, A16,
+                               A16, need, S0) == moe.MOE_ERR_UNSUPPORTED
+    # k = MOE_MAX_TOPK stays accepted up to the workspace check
+    k = moe.MOE_MAX_TOPK
+    need = moe.moe_dispatch_workspace_bytes(T, E, k)
+    assert lib.moe_dispatch_layout(A16, T, k, E, N, ctypes.byref(o), A16, need - 1, S0) == \
+        moe.MOE_ERR_WORKSPACE
+
+
 def test_ep_capacity_and_validation():
     lib = moe.load()
     assert lib.moe_ep_capacity(512, 384, 8, 8) == 512 * 8

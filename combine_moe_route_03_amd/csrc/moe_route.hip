@@ -335,6 +335,33 @@ __global__ __launch_bounds__(kThreads) void k_route_topk_wide(const float* __res
     route_token<PL>(logits + t * E, E, k, topk_idx + t * k, topk_w + t * k);
 }
 
+// The counts of routing block b, popcount(mask[e]), stored block-major: as u32 at hist[b*E + e],
+// or, with hist8 non-null, as one byte each at hist8[b*E16 + e], the row padded with zeros to E16
+// (E rounded up to 16). A block holds 16 tokens and a routed token names an expert at most once,
+// so a count is at most 16 and fits a byte; the whole table (96 KB for 4096 tokens and 384
+// experts) is then small enough for every rows workgroup to sum it itself (k_layout_rows8).
+__device__ __forceinline__ void store_block_counts(const uint32_t* mask, int32_t E, int64_t b,
+                                                   uint32_t* __restrict__ hist,
+                                                   uint8_t* __restrict__ hist8, int32_t E16)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    if (hist8 != nullptr) {
+        uint32_t* row = reinterpret_cast<uint32_t*>(hist8 + b * E16);
+        for (int q = tid; q < E16 / 4; q += nt) {
+            uint32_t packed = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = 4 * q + j;
+                packed |= (e < E ? (uint32_t)__popc(mask[e]) : 0u) << (8 * j);
+            }
+            row[q] = packed;
+        }
+    } else {
+        for (int e = tid; e < E; e += nt)
+            hist[b * E + e] = (uint32_t)__popc(mask[e]);
+    }
+}
+
 // Routing plus the counting half of dispatch in one launch, one wavefront per token (used for
 // k > 16). Workgroup b routes tokens
 // 16b .. 16b+15 (wavefront w takes token 16b + w); each selected (token, slot) sets bit w of
@@ -346,7 +373,7 @@ template <int PL>
 __global__ __launch_bounds__(kGroupThreads) void k_route_layout_wide(
     const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ local_rank)
+    uint32_t* __restrict__ local_rank, uint8_t* __restrict__ hist8, int32_t E16)
 {
     extern __shared__ uint32_t lds_mask[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -363,8 +390,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_layout_wide(
     __syncthreads();
     if (my_id >= 0)
         local_rank[t * k + lane] = (uint32_t)__popc(lds_mask[my_id] & ((1u << wave) - 1u));
-    for (int e = tid; e < E; e += kGroupThreads)
-        hist[(int64_t)blockIdx.x * E + e] = (uint32_t)__popc(lds_mask[e]);
+    store_block_counts(lds_mask, E, blockIdx.x, hist, hist8, E16);
 }
 
 // ------------------------------------------------------------------------ x prefetch --
@@ -545,7 +571,8 @@ template <int P>
 __global__ __launch_bounds__(kThreads) void k_route_layout(
     const float* __restrict__ logits, int32_t T, int32_t E, int32_t k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ local_rank, int32_t nblk, Prefetch pf)
+    uint32_t* __restrict__ local_rank, int32_t nblk, Prefetch pf, uint8_t* __restrict__ hist8,
+    int32_t E16)
 {
     if ((int32_t)blockIdx.x >= nblk) {                   // uniform per workgroup, before barriers
         prefetch_span(pf, (int)blockIdx.x - nblk);
@@ -567,8 +594,7 @@ __global__ __launch_bounds__(kThreads) void k_route_layout(
     __syncthreads();
     if (my_id >= 0)
         local_rank[t * k + l16] = (uint32_t)__popc(lds_mask32[my_id] & ((1u << q) - 1u));
-    for (int e = tid; e < E; e += kThreads)
-        hist[(int64_t)blockIdx.x * E + e] = (uint32_t)__popc(lds_mask32[e]);
+    store_block_counts(lds_mask32, E, blockIdx.x, hist, hist8, E16);
 }
 
 // --------------------------------------------------------------------------------- layout --
@@ -838,6 +864,298 @@ __global__ __launch_bounds__(kThreads) void k_layout_rows(RowPlan rp, int32_t R,
     }
     rp.token_row[i] = row;
     if (!ep && (uint32_t)row < (uint32_t)R)
+        rp.row_token[row] = t;
+    if (i - w0 >= (int64_t)window_rows)                  // past the window's valid rows
+        rp.list[i] = make_int2(-1, -1);
+}
+
+// Rows of routed items without a separate scan launch. The routing launch stores the blocks'
+// counts as bytes, block-major (store_block_counts), and every workgroup of this launch sums the
+// whole table itself: e's total, e's rows in the blocks before the workgroup's window, and the
+// exclusive prefix of e's counts over the window's blocks. Workgroup g of window w then takes
+// kRows8Threads items of the window; item i of block b with expert e takes
+//   row = expert_offset[e] + before_window[e] + in_window_prefix[b][e] + local_rank[i]
+// and list position qbase[e] + in_window_prefix[b][e] + local_rank[i] of its window, qbase[e]
+// being the window's rows of lower experts. Outputs are those of k_layout_rows (without the
+// expert-parallel mode).
+//
+// Summing the table: a 16-lane DPP row takes one 16-byte column c (16 experts) and lane l of it
+// the table rows l, l + 16, l + 32, ...: every load instruction of a wavefront reads 16 rows x 64
+// contiguous bytes, all loads of a lane are issued at once, and the bytes are added as pairs of
+// 16-bit lanes (even and odd bytes of each word; no sum reaches 2^16: a count is at most 16 and a
+// total at most the token count). Reductions over the 16 lanes of a row are DPP butterflies, and
+// the window's prefixes a DPP row scan with a carry from one group of 16 rows to the next, so no
+// value goes through LDS before the per-expert results. LDS (dynamic): wpre [bpw][E16] u16, then
+// tot, pre, wcnt, eoff, qbase [E16] u32. Workgroups from `groups` on read x ahead for packing.
+constexpr int kRows8Threads = 512;
+constexpr int kRows8Waves = kRows8Threads / 64;
+constexpr int kRows8Batch = 16;                    // table rows a lane loads at once
+
+struct RowPlan8 {
+    const int32_t* topk_idx;
+    const uint32_t* local_rank;
+    const uint8_t* hist8;     // [nblk][E16] counts
+    int32_t* token_row;
+    int32_t* row_token;
+    int2* list;
+    int32_t E, E16, nblk, rows_per_block;
+    int32_t blocks_per_window, groups_per_window;
+};
+
+// Pairs of bytes of 16 experts in 16-bit lanes: p[j] holds experts 4j and 4j + 2 of the column
+// (low, high half), p[4 + j] experts 4j + 1 and 4j + 3.
+struct BytePairs {
+    uint32_t p[8];
+};
+
+__device__ __forceinline__ void add_pairs(BytePairs& a, const u32x4& v)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a.p[j] += w[j] & 0x00FF00FFu;
+        a.p[4 + j] += (w[j] >> 8) & 0x00FF00FFu;
+    }
+}
+
+// Sum over the 16 lanes of each DPP row, in every lane of the row.
+__device__ __forceinline__ void row16_sum(BytePairs& a)
+{
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        uint32_t v = a.p[q];
+        v += dpp_u32<kDppQuadXor1>(v);
+        v += dpp_u32<kDppQuadXor2>(v);
+        v += dpp_u32<kDppRowHalfMirror>(v);
+        v += dpp_u32<kDppRowMirror>(v);
+        a.p[q] = v;
+    }
+}
+
+// Inclusive prefix over the lanes of each DPP row (lanes before the row's start add 0).
+__device__ __forceinline__ void row16_inclusive(BytePairs& a)
+{
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        uint32_t v = a.p[q];
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // shr:1
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // shr:2
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // shr:4
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // shr:8
+        a.p[q] = v;
+    }
+}
+
+// The 16-bit value of expert x (0..15) of the column.
+__device__ __forceinline__ uint32_t pair_value(const BytePairs& a, int x)
+{
+    const int j = x >> 2, q = x & 3;
+    uint32_t w = 0u;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+        w = (jj == j) ? ((q & 1) ? a.p[4 + jj] : a.p[jj]) : w;
+    return (q & 2) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// The 16 values in expert order as 16-bit words (two 16-byte stores).
+__device__ __forceinline__ void store_pairs_u16(uint16_t* dst, const BytePairs& a)
+{
+    u32x4 lo, hi;
+    lo.x = (a.p[0] & 0xFFFFu) | (a.p[4] << 16);
+    lo.y = (a.p[0] >> 16) | (a.p[4] & 0xFFFF0000u);
+    lo.z = (a.p[1] & 0xFFFFu) | (a.p[5] << 16);
+    lo.w = (a.p[1] >> 16) | (a.p[5] & 0xFFFF0000u);
+    hi.x = (a.p[2] & 0xFFFFu) | (a.p[6] << 16);
+    hi.y = (a.p[2] >> 16) | (a.p[6] & 0xFFFF0000u);
+    hi.z = (a.p[3] & 0xFFFFu) | (a.p[7] << 16);
+    hi.w = (a.p[3] >> 16) | (a.p[7] & 0xFFFF0000u);
+    reinterpret_cast<u32x4*>(dst)[0] = lo;
+    reinterpret_cast<u32x4*>(dst)[1] = hi;
+}
+
+// Two exclusive scans over the block at once (one value of each per thread), one barrier.
+template <int NT>
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t* wave_tot,
+                                                      uint32_t& ea, uint32_t& eb, uint32_t& ta,
+                                                      uint32_t& tb)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t ia = wave_inclusive_scan_u32(a), ib = wave_inclusive_scan_u32(b);
+    if (lane == 63) {
+        wave_tot[2 * wave] = ia;
+        wave_tot[2 * wave + 1] = ib;
+    }
+    __syncthreads();
+    uint32_t ba = 0u, bb = 0u;
+    ta = 0u;
+    tb = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t sa = wave_tot[2 * w], sb = wave_tot[2 * w + 1];
+        ba += (w < wave) ? sa : 0u;
+        bb += (w < wave) ? sb : 0u;
+        ta += sa;
+        tb += sb;
+    }
+    ea = ba + ia - a;
+    eb = bb + ib - b;
+}
+
+__global__ __launch_bounds__(kRows8Threads) void k_layout_rows8(RowPlan8 rp, int32_t R, int32_t k,
+                                                                CountOutputs co, int32_t groups,
+                                                                Prefetch pf)
+{
+    if ((int32_t)blockIdx.x >= groups) {                 // uniform per workgroup, before barriers
+        prefetch_span(pf, (int)blockIdx.x - groups);
+        return;
+    }
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_r8[];
+    __shared__ uint32_t wave_tot[2 * kRows8Waves];
+    const int tid = threadIdx.x, E = rp.E, E16 = rp.E16, bpw = rp.blocks_per_window;
+    uint16_t* wpre = reinterpret_cast<uint16_t*>(lds_r8);                        // [bpw][E16]
+    uint32_t* tot = reinterpret_cast<uint32_t*>(lds_r8 + (int64_t)2 * bpw * E16);
+    uint32_t* pre = tot + E16;                                                    // [E16]
+    uint32_t* wcnt = pre + E16;                                                   // [E16]
+    uint32_t* eoff = wcnt + E16;                                                  // [E16]
+    uint32_t* qbase = eoff + E16;                                                 // [E16]
+    const int w = blockIdx.x / rp.groups_per_window;
+    const int g = blockIdx.x - w * rp.groups_per_window;
+    const int b0 = w * bpw;
+    const int b1 = min(b0 + bpw, rp.nblk);
+    const int64_t w0 = (int64_t)b0 * rp.rows_per_block;
+    const int64_t w1 = min((int64_t)b1 * rp.rows_per_block, (int64_t)R);
+    const int64_t i = w0 + (int64_t)g * kRows8Threads + tid;
+    const bool item = b0 < rp.nblk && i < w1;
+    int e_i = -1;
+    uint32_t lr = 0u;
+    if (item) {                                          // in flight while the table is summed
+        e_i = rp.topk_idx[i];
+        lr = rp.local_rank[i];
+    }
+
+    // the table: DPP row d of the workgroup takes columns d, d + 32, ...; lane l16 the rows
+    // l16, l16 + 16, ... (every lane of a wavefront runs the same iterations)
+    const int C = E16 / 16, l16 = tid & 15;
+    const int passes = (C + kRows8Threads / 16 - 1) / (kRows8Threads / 16);
+    const u32x4* h = reinterpret_cast<const u32x4*>(rp.hist8);
+    for (int pass = 0; pass < passes; ++pass) {
+        const int c = (tid >> 4) + pass * (kRows8Threads / 16);
+        const bool col = c < C;                          // uniform per DPP row
+        BytePairs all = {}, bef = {}, carry = {};
+        for (int r0 = 0; r0 < rp.nblk; r0 += 16 * kRows8Batch) {   // uniform
+            u32x4 v[kRows8Batch];
+#pragma unroll
+            for (int u = 0; u < kRows8Batch; ++u) {
+                const int r = r0 + 16 * u + l16;
+                v[u] = (col && r < rp.nblk) ? h[(int64_t)r * C + c] : u32x4{0u, 0u, 0u, 0u};
+            }
+            // 8 rows at a time as plain bytes (a byte sum of 8 counts <= 16 stays below 256),
+            // then widened once into the 16-bit pairs
+#pragma unroll
+            for (int u0 = 0; u0 < kRows8Batch; u0 += 8) {
+                const int rlo = r0 + 16 * u0, rhi = r0 + 16 * (u0 + 8);   // rows [rlo, rhi)
+                u32x4 acc = v[u0];
+#pragma unroll
+                for (int u = u0 + 1; u < u0 + 8; ++u)
+                    acc += v[u];
+                add_pairs(all, acc);
+                if (rhi <= b0) {                         // every row before the window (uniform)
+                    add_pairs(bef, acc);
+                } else if (rlo < b0) {                   // the chunk holding b0 (uniform)
+                    u32x4 part = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int u = u0; u < u0 + 8; ++u)
+                        if (r0 + 16 * u + l16 < b0)
+                            part += v[u];
+                    add_pairs(bef, part);
+                }
+            }
+        }
+        // the window's rows again (from cache), 16 at a time: row scan plus the carry so far
+        for (int rb = b0 & ~15; rb < b1; rb += 16) {     // uniform
+            const int r = rb + l16;
+            const bool in = col && r >= b0 && r < b1;
+            BytePairs x = {};
+            if (in)
+                add_pairs(x, h[(int64_t)r * C + c]);
+            BytePairs incl = x, grp = x;
+            row16_inclusive(incl);
+            row16_sum(grp);
+            if (in) {
+                BytePairs ex;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    ex.p[q] = carry.p[q] + incl.p[q] - x.p[q];
+                store_pairs_u16(wpre + (int64_t)(r - b0) * E16 + 16 * c, ex);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                carry.p[q] += grp.p[q];
+        }
+        row16_sum(all);
+        row16_sum(bef);
+        if (col) {                                       // lane l16 writes expert 16c + l16
+            const int e = 16 * c + l16;
+            tot[e] = pair_value(all, l16);
+            pre[e] = pair_value(bef, l16);
+            wcnt[e] = pair_value(carry, l16);
+        }
+    }
+    __syncthreads();
+
+    // expert offsets and the window's list bases; thread u takes experts 2u and 2u + 1
+    // (E16 <= 2 * kRows8Threads)
+    uint32_t tc[2] = {0u, 0u}, wc[2] = {0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = 2 * tid + u;
+        if (e < E16) {
+            tc[u] = tot[e];
+            wc[u] = wcnt[e];
+        }
+    }
+    uint32_t ex, qx, total, window_rows;
+    block_exclusive_scan2<kRows8Threads>(tc[0] + tc[1], wc[0] + wc[1], wave_tot, ex, qx, total,
+                                         window_rows);
+    if (2 * tid < E16) {
+        eoff[2 * tid] = ex;
+        qbase[2 * tid] = qx;
+    }
+    if (2 * tid + 1 < E16) {
+        eoff[2 * tid + 1] = ex + tc[0];
+        qbase[2 * tid + 1] = qx + wc[0];
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        const int epr = E / co.N;
+        for (int e = tid; e < E; e += kRows8Threads) {
+            co.expert_offsets[e] = (int32_t)eoff[e];
+            co.expert_counts[e] = (int32_t)tot[e];
+        }
+        for (int r = tid; r < co.N; r += kRows8Threads) {
+            co.rank_offsets[r] = (int32_t)eoff[r * epr];
+            uint32_t n = 0u;
+            for (int e = r * epr; e < (r + 1) * epr; ++e)
+                n += tot[e];
+            co.rank_counts[r] = (int32_t)n;
+        }
+        if (tid == 0) {
+            co.expert_offsets[E] = (int32_t)total;
+            co.rank_offsets[co.N] = (int32_t)total;
+        }
+    }
+    if (!item)
+        return;
+    const int32_t t = (int32_t)(i / k);
+    int32_t row = -1;
+    if ((uint32_t)e_i < (uint32_t)E) {
+        const int bi = (int)(i / rp.rows_per_block) - b0;
+        const uint32_t inw = (uint32_t)wpre[bi * E16 + e_i] + lr;
+        row = (int32_t)(eoff[e_i] + pre[e_i] + inw);
+        rp.list[w0 + (int64_t)(qbase[e_i] + inw)] = make_int2(row, t);
+    }
+    rp.token_row[i] = row;
+    if ((uint32_t)row < (uint32_t)R)
         rp.row_token[row] = t;
     if (i - w0 >= (int64_t)window_rows)                  // past the window's valid rows
         rp.list[i] = make_int2(-1, -1);
@@ -1774,6 +2092,7 @@ struct Workspace {
     uint32_t* totals;
     uint32_t* local_rank;
     int2* list;
+    uint8_t* hist8;          // routing blocks' byte counts (k_layout_rows8), in the prefix piece
 };
 
 inline int64_t ws_nblk(int32_t T, int32_t k)
@@ -1784,10 +2103,15 @@ inline int64_t ws_nblk(int32_t T, int32_t k)
     return n;
 }
 
-// The histograms of the largest layout plan, plus one word (the prefetch's sink).
+inline int32_t e16(int32_t E) { return (int32_t)align_up((size_t)E, 16); }
+
+// The histograms of the largest layout plan, plus one word (the prefetch's sink); also large
+// enough for the byte counts of the routing blocks (nblk rows of E16 bytes, in the prefix piece).
 inline size_t ws_hist_bytes(int32_t T, int32_t E, int32_t k)
 {
-    return align_up(((size_t)ws_nblk(T, k) * E + 1) * sizeof(uint32_t), 256);
+    const size_t words = ((size_t)ws_nblk(T, k) * E + 1) * sizeof(uint32_t);
+    const size_t bytes8 = (size_t)ws_nblk(T, k) * e16(E);
+    return align_up(words > bytes8 ? words : bytes8, 256);
 }
 
 inline size_t ws_bytes(int32_t T, int32_t E, int32_t k)
@@ -1807,6 +2131,7 @@ inline Workspace carve_workspace(void* base, int32_t T, int32_t E, int32_t k)
     w.hist = reinterpret_cast<uint32_t*>(p);
     w.sink = w.hist + ws_nblk(T, k) * E;
     w.prefix = reinterpret_cast<uint32_t*>(p + hb);
+    w.hist8 = reinterpret_cast<uint8_t*>(p + hb);
     w.totals = reinterpret_cast<uint32_t*>(p + 2 * hb);
     w.local_rank = reinterpret_cast<uint32_t*>(p + 2 * hb + tb);
     const int64_t R = (int64_t)T * k;
@@ -1997,19 +2322,24 @@ Prefetch make_prefetch(const void* x, int64_t x_bytes, const Workspace& ws, int 
 
 
 
+// Routing and counting; with bytes8 the block counts go out as bytes (ws.hist8) for
+// k_layout_rows8, else as u32 (ws.hist) for the scan.
 void launch_route_layout(const float* logits, int32_t T, int32_t E, int32_t k,
                          int32_t* topk_idx, float* topk_w, const Workspace& ws,
-                         const LayoutPlan& plan, const Prefetch& pf, hipStream_t stream)
+                         const LayoutPlan& plan, const Prefetch& pf, bool bytes8,
+                         hipStream_t stream)
 {
+    uint8_t* h8 = bytes8 ? ws.hist8 : nullptr;
     if (route_rows16(T, k)) {
         const dim3 grid((unsigned)(plan.nblk + pf.groups));
         MOE_ROUTE16_LAUNCH(k_route_layout, grid, kThreads, (size_t)E * sizeof(uint32_t), logits,
-                           T, E, k, topk_idx, topk_w, ws.hist, ws.local_rank, plan.nblk, pf);
+                           T, E, k, topk_idx, topk_w, ws.hist, ws.local_rank, plan.nblk, pf, h8,
+                           e16(E));
         return;
     }
     const dim3 grid((unsigned)plan.nblk);               // wavefront a token: no prefetch
     MOE_ROUTE_LAUNCH(k_route_layout_wide, grid, kGroupThreads, (size_t)E * sizeof(uint32_t),
-                     logits, T, E, k, topk_idx, topk_w, ws.hist, ws.local_rank);
+                     logits, T, E, k, topk_idx, topk_w, ws.hist, ws.local_rank, h8, e16(E));
 }
 
 void launch_hist(const int32_t* topk_idx, int64_t R, int32_t E, const Workspace& ws,
@@ -2084,6 +2414,46 @@ void launch_scan_rows(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E,
     const int32_t rows_groups = (int32_t)(want < 1 ? 1 : want);
     k_layout_rows<<<(unsigned)(rows_groups + pf_rows.groups), kThreads, 0, stream>>>(
         rp, R, k, co, rows_groups, pf_rows);
+}
+
+// The rows of routed items in one launch after routing (k_layout_rows8): taken when every
+// workgroup can sum the whole byte-count table quickly and the window's part fits LDS.
+constexpr int64_t kRows8TableBytes = 256 * 1024;
+constexpr int64_t kRows8WindowBytes = 40 * 1024;
+
+inline bool rows8_fits(const LayoutPlan& plan, const WindowPlan& wp, int32_t E)
+{
+    return (int64_t)plan.nblk * e16(E) <= kRows8TableBytes &&
+           (int64_t)2 * wp.blocks_per_window * e16(E) <= kRows8WindowBytes;
+}
+
+inline size_t rows8_lds_bytes(const WindowPlan& wp, int32_t E)
+{
+    return (size_t)2 * wp.blocks_per_window * e16(E) + (size_t)5 * e16(E) * 4;
+}
+
+void launch_rows8(const int32_t* topk_idx, int32_t R, int32_t k, int32_t E, int32_t* token_row,
+                  int32_t* row_token, const CountOutputs& co, const Workspace& ws,
+                  const LayoutPlan& plan, const WindowPlan& wp, const Prefetch& pf,
+                  hipStream_t stream)
+{
+    RowPlan8 rp;
+    rp.topk_idx = topk_idx;
+    rp.local_rank = ws.local_rank;
+    rp.hist8 = ws.hist8;
+    rp.token_row = token_row;
+    rp.row_token = row_token;
+    rp.list = ws.list;
+    rp.E = E;
+    rp.E16 = e16(E);
+    rp.nblk = plan.nblk;
+    rp.rows_per_block = plan.rows_per_block;
+    rp.blocks_per_window = wp.blocks_per_window;
+    rp.groups_per_window = (int32_t)ceil_div(wp.rows_per_window, kRows8Threads);
+    const int64_t want = (int64_t)wp.nwin * rp.groups_per_window;
+    const int32_t rows_groups = (int32_t)(want < 1 ? 1 : want);
+    k_layout_rows8<<<(unsigned)(rows_groups + pf.groups), kRows8Threads,
+                     rows8_lds_bytes(wp, E), stream>>>(rp, R, k, co, rows_groups, pf);
 }
 
 // Packing in token order (token_row given), or by windows from the list the rows kernel wrote.
@@ -2404,34 +2774,44 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     }
     const Workspace ws = carve_workspace(workspace, T, E, k);
     const int64_t x_bytes = (int64_t)T * H * (int64_t)dtype_size(x_dtype);
-    LayoutPlan plan;
-    // x is read ahead by the counting, scan and rows launches, a third each by default. The
-    // 16-lane routing-and-counting launch of many experts (E >= 256: 16 or more keys a lane) runs
-    // longest and takes half, scan and rows a quarter each (prefill step 189.6 against 190.9 us;
-    // the skewed batch of 128 experts is 0.5 us slower that way, so it keeps thirds). The
-    // wavefront-per-token routing launch (k > 16 or small batches) carries none, and scan and
-    // rows take halves.
+    const int64_t row_bytes = (int64_t)H * (int64_t)dtype_size(x_dtype);
     const bool fused = T > 0 && fused_route_fits(T, k);
     const bool wide = fused && !route_rows16(T, k);
-    const bool long_route = fused && !wide && E >= 256;
-    const int parts = wide ? 2 : (long_route ? 4 : 3);
-    const int q_route = wide ? 0 : (long_route ? 2 : 1);    // parts of each launch, in order
-    const Prefetch pf_route = make_prefetch(x, x_bytes, ws, 0, parts, q_route);
-    const Prefetch pf_scan = make_prefetch(x, x_bytes, ws, q_route, parts, 1);
-    const Prefetch pf_rows = make_prefetch(x, x_bytes, ws, q_route + 1, parts, 1);
-    if (fused) {
-        plan = route_plan(T, k);
-        launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan, pf_route, stream);
+    const LayoutPlan plan = fused ? route_plan(T, k) : hist_plan(R);
+    const WindowPlan wp = window_plan(plan, row_bytes, k);
+    if (fused && rows8_fits(plan, wp, E)) {
+        // two layout launches: routing with counting (byte counts), then the rows, each reading
+        // half of x ahead; the wavefront-per-token routing launch carries none, and the rows
+        // launch reads all of it
+        const Prefetch pf_route = wide ? no_prefetch() : make_prefetch(x, x_bytes, ws, 0, 2);
+        const Prefetch pf_rows = wide ? make_prefetch(x, x_bytes, ws, 0, 1)
+                                      : make_prefetch(x, x_bytes, ws, 1, 2);
+        launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan, pf_route, true, stream);
+        launch_rows8(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
+                     count_outputs(out, n_ranks), ws, plan, wp, pf_rows, stream);
     } else {
-        plan = hist_plan(R);
-        if (T > 0)
-            launch_route(logits, T, E, k, topk_idx, topk_w, stream);
-        launch_hist(topk_idx, R, E, ws, plan, pf_route, stream);
+        // x is read ahead by the counting, scan and rows launches, a third each by default. The
+        // 16-lane routing-and-counting launch of many experts (E >= 256: 16 or more keys a lane)
+        // runs longest and takes half, scan and rows a quarter each. The wavefront-per-token
+        // routing launch (k > 16 or small batches) carries none, and scan and rows take halves.
+        const bool long_route = fused && !wide && E >= 256;
+        const int parts = wide ? 2 : (long_route ? 4 : 3);
+        const int q_route = wide ? 0 : (long_route ? 2 : 1);    // parts of each launch, in order
+        const Prefetch pf_route = make_prefetch(x, x_bytes, ws, 0, parts, q_route);
+        const Prefetch pf_scan = make_prefetch(x, x_bytes, ws, q_route, parts, 1);
+        const Prefetch pf_rows = make_prefetch(x, x_bytes, ws, q_route + 1, parts, 1);
+        if (fused) {
+            launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan, pf_route, false,
+                                stream);
+        } else {
+            if (T > 0)
+                launch_route(logits, T, E, k, topk_idx, topk_w, stream);
+            launch_hist(topk_idx, R, E, ws, plan, pf_route, stream);
+        }
+        launch_scan_rows(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
+                         count_outputs(out, n_ranks), nullptr, ws, plan, wp, pf_scan, pf_rows,
+                         stream);
     }
-    const WindowPlan wp = window_plan(plan, (int64_t)H * (int64_t)dtype_size(x_dtype), k);
-    launch_scan_rows(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
-                     count_outputs(out, n_ranks), nullptr, ws, plan, wp, pf_scan, pf_rows,
-                     stream);
     launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
                 out->recv_scales, R, stream);
     return launch_status();

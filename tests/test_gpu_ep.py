@@ -19,7 +19,7 @@ def _announce(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
-def _run(w: EpWorkload, sample_rows: int = 0):
+def _run(w: EpWorkload):
     inp = make_inputs(w.as_workload())
     x, logits = inp["x"], inp["logits"]
     idx, wt = oracle.route(logits, w.k)
@@ -73,14 +73,11 @@ def _run(w: EpWorkload, sample_rows: int = 0):
     torch.cuda.synchronize()
     # compare
     assert np.array_equal(to_host(counts), o_counts), "region counts differ"
-    g_regions = to_host(regions)
-    g_returns = to_host(returns)
+    # the whole region and return arrays: every written row, and the untouched rows still zero
+    assert np.array_equal(to_host(regions), o_regions), "region rows differ"
+    assert np.array_equal(to_host(returns), o_returns), "returned rows differ"
     for s in range(S):
-        gr = to_host(rows[s])
-        assert np.array_equal(gr, o_rows[s]), f"send_row of source {s} differs"
-        used = gr if not sample_rows else gr[:: max(1, len(gr) // sample_rows)]
-        assert np.array_equal(g_regions[used], o_regions[used]), f"rows of source {s} differ"
-        assert np.array_equal(g_returns[used], o_returns[used]), f"returns of source {s} differ"
+        assert np.array_equal(to_host(rows[s]), o_rows[s]), f"send_row of source {s} differs"
         assert_close_out(to_host(outs[s]), o_out[s], w.dtype)
     for r in range(N):
         g, ec, eo, gs = (to_host(t) for t in recv[r])
@@ -88,8 +85,8 @@ def _run(w: EpWorkload, sample_rows: int = 0):
         assert np.array_equal(ec, o_recv[r]["expert_counts"]), f"rank {r} counts differ"
         assert np.array_equal(eo, o_recv[r]["expert_offsets"]), f"rank {r} offsets differ"
         assert np.array_equal(gs, o_recv[r]["grouped_src"]), f"rank {r} grouped_src differs"
-        sel = np.arange(n) if not sample_rows else np.arange(0, n, max(1, n // sample_rows))
-        assert np.array_equal(g[sel], o_recv[r]["grouped"][sel]), f"rank {r} grouped rows differ"
+        assert n <= len(g)
+        assert np.array_equal(g, o_recv[r]["grouped"]), f"rank {r} grouped rows differ"
     return dict(x_d=x_d, idx_d=idx_d, w_d=w_d, recv=recv, rows=rows, o_y=o_y, o_recv=o_recv,
                 o_rows=o_rows, idx=idx, wt=wt, o_out=o_out)
 
@@ -105,10 +102,12 @@ def test_ep_send_recv_return_combine(name):
     _run(w)
 
 
-def test_ep_prefill_sampled_rows():
+def test_ep_prefill_every_row():
+    """The prefill batch spread over 8 sources: every payload row of every region, return and
+    grouped layout compared in full."""
     w = EP_WORKLOADS["ep_prefill"]
     _announce(f"ep prefill S={w.S} T={w.T} H={w.H} E={w.E} k={w.k} N={w.N} cap={w.cap}")
-    _run(w, sample_rows=2048)
+    _run(w)
 
 
 def test_ep_grouped_layout_equals_dispatch_of_the_concatenated_batch():

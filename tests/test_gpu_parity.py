@@ -166,6 +166,10 @@ EDGE = [
     (700, 2056, 64, 4, 8, "bf16", "bf16"),      # a wavefront a token (T < 1024), ragged row tail
     (1100, 256, 384, 20, 48, "f32", "f32"),     # k > 16 past 1024 tokens
     (1024, 1024, 256, 8, 32, "bf16", "fp8_e4m3"),   # fp8 packing after the multi-launch layout
+    # routed rows from the byte-count table (two layout launches): E padded to 16 in the table,
+    # a partial last block; and many windows of few blocks with fp8 from fp32
+    (1500, 264, 100, 6, 5, "bf16", "bf16"),
+    (2100, 128, 520, 4, 8, "f32", "fp8_e4m3"),
     # layout folded into packing (up to 512 tokens through moe_route_dispatch)
     (100, 4104, 64, 4, 8, "bf16", "bf16"),      # ragged 16-byte tail, tokens across 4 mask words
     (200, 256, 384, 32, 48, "f32", "f32"),      # k > 16 (a wavefront a token in routing)
@@ -401,8 +405,8 @@ def test_one_dirty_workspace_serves_shapes_of_every_path():
     """The workspace needs no initialisation and may be larger than asked for: one buffer, filled
     with 0xFF bytes, serves in turn the multi-launch paths (routed: thirds of x read ahead; wide
     routing: halves; caller-given ids) and the one-launch paths, each output equal to the oracle's."""
-    shapes = [(4096, 1024, 384, 8, 48, "bf16"),    # 16 lanes a token, read-ahead in thirds
-              (700, 2048, 64, 4, 8, "bf16"),       # a wavefront a token: read-ahead in halves
+    shapes = [(4096, 1024, 384, 8, 48, "bf16"),    # 16 lanes a token, byte-count rows launch
+              (700, 2048, 64, 4, 8, "bf16"),       # a wavefront a token: x read ahead by the rows launch
               (1100, 512, 384, 20, 48, "f32"),     # k > 16 past 1024 tokens
               (300, 1024, 64, 4, 8, "bf16"),       # one launch for layout and packing
               (16, 256, 8, 2, 2, "f32")]           # routing in that launch too

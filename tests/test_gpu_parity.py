@@ -252,6 +252,48 @@ def test_all_tokens_on_one_expert_and_ties(T):
         _check_payload(buf, d, "f32")
 
 
+def _one_lane_logits(T, E, k, seed):
+    """Logits whose best experts sit in one lane of the 16-lane selection (experts L, L + 16, ...
+    for L = t % 16), with ties in pairs among them, so that one lane wins every slot of the token
+    in turn; every third token ties all E logits (the k lowest ids win)."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    for t in range(T):
+        if t % 3 == 2:
+            logits[t] = 0.0
+            continue
+        lane = t % 16
+        ids = np.arange(lane, E, 16)[:k + 3]
+        logits[t, ids] = (10.0 - (np.arange(len(ids)) // 2)).astype(np.float32)
+    return logits
+
+
+@pytest.mark.parametrize("T,E,k", [
+    (1100, 384, 8),     # 16 lanes a token, 24 keys a lane (routing launch of the layout)
+    (1030, 384, 16),    # every slot from one lane
+    (1024, 64, 12),     # four keys a lane: the cache holds them all
+    (20, 256, 16),      # routing inside the layout-and-pack launch
+    (300, 256, 8),      # a wavefront a token (below 1024 tokens)
+])
+def test_route_with_one_lane_holding_the_best_experts(T, E, k):
+    _announce(f"edge one-lane routing T={T} E={E} k={k}")
+    H, N = 128, 8
+    logits = _one_lane_logits(T, E, k, seed=T + E + k)
+    x = np.random.default_rng(1).standard_normal((T, H)).astype(np.float32)
+    idx, wt = oracle.route(logits, k)
+    d = oracle.dispatch(x, "f32", idx, E, N, "f32")
+    g_idx, g_w = moe.moe_route_topk(to_dev(logits, "f32"), k)
+    buf = moe.alloc_dispatch_out(T, H, E, k, N, "f32")
+    f_idx, f_w, _ = moe.moe_route_dispatch(to_dev(logits, "f32"), to_dev(x, "f32"), k, N, buf,
+                                           moe.alloc_workspace(T, E, k))
+    torch.cuda.synchronize()
+    for gi, gw in ((g_idx, g_w), (f_idx, f_w)):
+        assert np.array_equal(to_host(gi), idx)
+        _check_weights(to_host(gw), wt)
+    _check_layout(buf, d)
+    _check_payload(buf, d, "f32")
+
+
 @pytest.mark.parametrize("T,H,E,k,N,payload", [
     (600, 128, 16, 4, 4, "f32"),       # multi-launch layout
     (300, 128, 16, 4, 4, "f32"),       # one-launch layout, exact ranks

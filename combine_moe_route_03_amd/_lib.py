@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = r
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_MAX_EXPERTS = 1024
 MOE_MAX_TOPK = 64
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}
@@ -56,6 +57,7 @@ def load() -> ctypes.CDLL:
         lib.moe_dispatch_pack.argtypes = [P, I, I, I, I, P, I, P, P, P]
         lib.moe_dispatch.argtypes = [P, I, I, I, P, I, I, I, I, P, P, Z, P]
         lib.moe_route_dispatch.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, Z, P]
+        lib.moe_route_dispatch_noalloc.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P]
         lib.moe_combine.argtypes = [P, I, I, I, I, P, P, P, I, P]
         lib.moe_ep_capacity.argtypes = [I, I, I, I]
         lib.moe_ep_capacity.restype = ctypes.c_int64
@@ -70,7 +72,7 @@ def load() -> ctypes.CDLL:
         lib.moe_ep_combine_reduced.argtypes = [P, I, I, I, I, P, I, P, I, P]
         lib.moe_check_topk.argtypes = [P, I, I, I, P, P]
         for fn in ("moe_route_topk", "moe_dispatch_layout", "moe_dispatch_pack", "moe_dispatch",
-                   "moe_route_dispatch", "moe_combine", "moe_ep_send", "moe_ep_recv",
+                   "moe_route_dispatch", "moe_route_dispatch_noalloc", "moe_combine", "moe_ep_send", "moe_ep_recv",
                    "moe_ep_return", "moe_ep_combine", "moe_ep_partial_rows", "moe_ep_reduce",
                    "moe_ep_combine_reduced", "moe_check_topk"):
             getattr(lib, fn).restype = I
@@ -240,6 +242,26 @@ def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, n_ranks: i
         _ptr(logits), _ptr(x), _dtype_code(x), T, H, E, k, n_ranks,
         _dtype_code(out.recv, fp8_ok=True), _ptr(topk_idx), _ptr(topk_w), ctypes.byref(st),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return topk_idx, topk_w, out
+
+
+def moe_route_dispatch_noalloc(logits: torch.Tensor, x: torch.Tensor, k: int, n_ranks: int,
+                               out: DispatchBuffers, topk_idx: Optional[torch.Tensor] = None,
+                               topk_w: Optional[torch.Tensor] = None, stream=None):
+    """moe_route_dispatch with the library's fixed device scratch instead of a workspace (the
+    call allocates no device memory); returns (topk_idx, topk_w, out)."""
+    T, E = logits.shape
+    H = x.shape[1]
+    assert logits.dtype == torch.float32 and logits.is_contiguous() and x.shape[0] == T
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    st = out.as_struct()
+    _check("moe_route_dispatch_noalloc", load().moe_route_dispatch_noalloc(
+        _ptr(logits), _ptr(x), _dtype_code(x), T, H, E, k, n_ranks,
+        _dtype_code(out.recv, fp8_ok=True), _ptr(topk_idx), _ptr(topk_w), ctypes.byref(st),
+        _stream(stream)))
     return topk_idx, topk_w, out
 
 

@@ -42,6 +42,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe_route.h"
 
 namespace {
@@ -2030,6 +2032,13 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_ep_finish(
     Store8<OT>::run(out + t * H + (int64_t)c * 8, acc);
 }
 
+// ----------------------------------------------------------------- fixed device scratch --
+// The workspace of moe_route_dispatch_noalloc: device memory of the library itself, one array per
+// device, held until the process ends, so that the call allocates nothing. Host code never passes
+// `scratch` itself to a kernel (on the host the name is a stand-in, not a device address); the
+// device address comes from hipGetSymbolAddress (device_scratch).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 // ------------------------------------------------------------------------------ host helpers --
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -2738,11 +2747,15 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
     return launch_status();
 }
 
-moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t x_dtype,
-                                int32_t T, int32_t H, int32_t E, int32_t k, int32_t n_ranks,
-                                moe_dtype_t payload_dtype, int32_t* topk_idx, float* topk_w,
-                                const moe_dispatch_out_t* out, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+moe_status_t check_route_dispatch_args(const float* logits, const void* x, moe_dtype_t x_dtype,
+                                       int32_t T, int32_t H, int32_t E, int32_t k,
+                                       int32_t n_ranks, moe_dtype_t payload_dtype,
+                                       const int32_t* topk_idx, const float* topk_w,
+                                       const moe_dispatch_out_t* out)
 {
     moe_status_t st = check_route_args(logits, T, E, k, topk_idx, topk_w);
     if (st != MOE_OK)
@@ -2750,14 +2763,16 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     st = check_layout_args(topk_idx, T, k, E, n_ranks, out);
     if (st != MOE_OK)
         return st;
-    st = check_pack_args(x, x_dtype, T, H, k, out->token_row, payload_dtype, out->recv,
-                         out->recv_scales);
-    if (st != MOE_OK)
-        return st;
-    if (!workspace || workspace_bytes < moe_dispatch_workspace_bytes(T, E, k))
-        return MOE_ERR_WORKSPACE;
-    if (!aligned(workspace, 16))
-        return MOE_ERR_UNSUPPORTED;
+    return check_pack_args(x, x_dtype, T, H, k, out->token_row, payload_dtype, out->recv,
+                           out->recv_scales);
+}
+
+// Routing and dispatch once the arguments and the workspace are known to be valid.
+moe_status_t route_dispatch(const float* logits, const void* x, moe_dtype_t x_dtype, int32_t T,
+                            int32_t H, int32_t E, int32_t k, int32_t n_ranks,
+                            moe_dtype_t payload_dtype, int32_t* topk_idx, float* topk_w,
+                            const moe_dispatch_out_t* out, void* workspace, hipStream_t stream)
+{
     const int64_t R = (int64_t)T * k;
     if (lp_route_fits(T, E, k)) {
         // the smallest batches: routing, layout and packing in one launch
@@ -2815,6 +2830,81 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
     launch_pack(x, x_dtype, T, H, k, out->token_row, ws.list, &wp, payload_dtype, out->recv,
                 out->recv_scales, R, stream);
     return launch_status();
+}
+
+// Device address of `scratch` on the device of `stream` (the current device for the null
+// stream): looked up once per device with that device current, then kept.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxScratchDevices];
+
+moe_status_t device_scratch(hipStream_t stream, void** addr)
+{
+    int dev = 0;
+    const hipError_t ge = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (ge != hipSuccess)
+        return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess)
+            return MOE_ERR_HIP;
+        void* p = nullptr;
+        const hipError_t se = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (se != hipSuccess || p == nullptr)
+            return MOE_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t x_dtype,
+                                int32_t T, int32_t H, int32_t E, int32_t k, int32_t n_ranks,
+                                moe_dtype_t payload_dtype, int32_t* topk_idx, float* topk_w,
+                                const moe_dispatch_out_t* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    const moe_status_t st = check_route_dispatch_args(logits, x, x_dtype, T, H, E, k, n_ranks,
+                                                      payload_dtype, topk_idx, topk_w, out);
+    if (st != MOE_OK)
+        return st;
+    if (!workspace || workspace_bytes < moe_dispatch_workspace_bytes(T, E, k))
+        return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return MOE_ERR_UNSUPPORTED;
+    return route_dispatch(logits, x, x_dtype, T, H, E, k, n_ranks, payload_dtype, topk_idx,
+                          topk_w, out, workspace, stream);
+}
+
+moe_status_t moe_route_dispatch_noalloc(const float* logits, const void* x, moe_dtype_t x_dtype,
+                                        int32_t T, int32_t H, int32_t E, int32_t k,
+                                        int32_t n_ranks, moe_dtype_t payload_dtype,
+                                        int32_t* topk_idx, float* topk_w,
+                                        const moe_dispatch_out_t* out, hipStream_t stream)
+{
+    moe_status_t st = check_route_dispatch_args(logits, x, x_dtype, T, H, E, k, n_ranks,
+                                                payload_dtype, topk_idx, topk_w, out);
+    if (st != MOE_OK)
+        return st;
+    if (moe_dispatch_workspace_bytes(T, E, k) > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = device_scratch(stream, &ws);
+    if (st != MOE_OK)
+        return st;
+    return route_dispatch(logits, x, x_dtype, T, H, E, k, n_ranks, payload_dtype, topk_idx,
+                          topk_w, out, ws, stream);
 }
 
 moe_status_t moe_check_topk(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,

@@ -154,6 +154,30 @@ moe_status_t moe_route_dispatch(const float* logits, const void* x, moe_dtype_t 
                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_route_dispatch_noalloc -- moe_route_dispatch without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). It allocates nothing: its workspace is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per device, held until the
+ * process ends (its address on a device is looked up on the first call there).
+ *   Arguments, outputs and argument errors are those of moe_route_dispatch; every output equals
+ *   what moe_route_dispatch writes. A call that needs more than MOE_NOALLOC_SCRATCH_BYTES of
+ *   workspace (moe_dispatch_workspace_bytes(T, E, k) > MOE_NOALLOC_SCRATCH_BYTES) returns
+ *   MOE_ERR_WORKSPACE before anything is enqueued; MOE_ERR_HIP if the array's address cannot be
+ *   had on the stream's device.
+ *   All calls on one device share that device's array, and a call leaves its contents behind (no
+ *   call reads what another wrote before writing it itself). Calls on one device whose work may
+ *   overlap in time (different streams without ordering between them) race on the array and give
+ *   undefined results: order them on one stream, or use moe_route_dispatch with a workspace each.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+moe_status_t moe_route_dispatch_noalloc(const float* logits, const void* x, moe_dtype_t x_dtype,
+                                        int32_t T, int32_t H, int32_t E, int32_t k,
+                                        int32_t n_ranks, moe_dtype_t payload_dtype,
+                                        int32_t* topk_idx, float* topk_w,
+                                        const moe_dispatch_out_t* out, hipStream_t stream);
+
+/*
  * moe_combine -- weighted sum of the returned rows of every token ("Dispatch en Combine": the
  * receiver accumulates the rows from its receive buffer into the output tensor; "Introductie":
  * combine forms their weighted average -- with renormalised weights that is this sum).

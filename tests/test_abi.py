@@ -28,7 +28,8 @@ def test_library_loads_and_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["moe_combine", "moe_dispatch", "moe_dispatch_layout",
                             "moe_dispatch_pack", "moe_dispatch_workspace_bytes",
-                            "moe_route_dispatch", "moe_route_topk", "moe_status_str",
+                            "moe_route_dispatch", "moe_route_dispatch_noalloc",
+                            "moe_route_topk", "moe_status_str",
                             "moe_ep_capacity", "moe_ep_send", "moe_ep_recv", "moe_ep_return",
                             "moe_ep_combine", "moe_ep_partial_rows",
                             "moe_ep_reduce_workspace_bytes", "moe_ep_reduce",
@@ -48,6 +49,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert f"#define MOE_MAX_EXPERTS {moe.MOE_MAX_EXPERTS}" in text
     assert f"#define MOE_MAX_TOPK {moe.MOE_MAX_TOPK}" in text
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
+    assert moe.MOE_NOALLOC_SCRATCH_BYTES == 16 << 20
     for name, val in [("MOE_F32", 0), ("MOE_BF16", 1), ("MOE_FP8_E4M3", 2), ("MOE_OK", 0),
                       ("MOE_ERR_INVALID", 1), ("MOE_ERR_UNSUPPORTED", 2),
                       ("MOE_ERR_WORKSPACE", 3), ("MOE_ERR_HIP", 4)]:
@@ -201,6 +204,35 @@ def test_layout_calls_reject_k_beyond_max_topk():
     need = moe.moe_dispatch_workspace_bytes(T, E, k)
     assert lib.moe_dispatch_layout(A16, T, k, E, N, ctypes.byref(o), A16, need - 1, S0) == \
         moe.MOE_ERR_WORKSPACE
+
+
+def test_route_dispatch_noalloc_validation():
+    """Argument errors are those of moe_route_dispatch, and a batch whose workspace exceeds the
+    fixed scratch is rejected, all before any device call (none is possible here)."""
+    f = moe.load().moe_route_dispatch_noalloc
+    o = _out_struct()
+    BF16, FP8 = moe.MOE_BF16, moe.MOE_FP8_E4M3
+    args = dict(logits=A16, x=A16, xd=BF16, T=4, H=256, E=8, k=2, N=2, pd=BF16, idx=A16b,
+                w=A16b, out=ctypes.byref(o))
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["logits"], a["x"], a["xd"], a["T"], a["H"], a["E"], a["k"], a["N"], a["pd"],
+                 a["idx"], a["w"], a["out"], S0)
+
+    assert call(k=9) == moe.MOE_ERR_INVALID                      # k > E
+    assert call(logits=None) == moe.MOE_ERR_INVALID
+    assert call(E=2048) == moe.MOE_ERR_UNSUPPORTED
+    assert call(N=3) == moe.MOE_ERR_INVALID                      # E % N
+    assert call(out=None) == moe.MOE_ERR_INVALID
+    assert call(x=MIS) == moe.MOE_ERR_UNSUPPORTED
+    assert call(H=192, pd=FP8) == moe.MOE_ERR_UNSUPPORTED
+    assert call(k=65, E=128) == moe.MOE_ERR_UNSUPPORTED
+    # the largest batches: beyond MOE_NOALLOC_SCRATCH_BYTES of workspace
+    T, E, k = 65536, 1024, 16
+    assert moe.moe_dispatch_workspace_bytes(T, E, k) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(T=T, E=E, k=k, N=8, H=128) == moe.MOE_ERR_WORKSPACE
+    assert moe.moe_dispatch_workspace_bytes(4096, 384, 8) <= moe.MOE_NOALLOC_SCRATCH_BYTES
 
 
 def test_ep_capacity_and_validation():

@@ -532,7 +532,8 @@ def main():
         del sets
         torch.cuda.empty_cache()
         print("[bench] other workloads", file=sys.stderr, flush=True)
-        others = other_workloads(torch, moe, dev, ("tiny", "decode", "decode_fp8", "skewed"),
+        others = other_workloads(torch, moe, dev,
+                                 ("tiny", "decode", "decode_fp8", "skewed", "prefill_fp8"),
                                  100, max(1, args.sets))
         print("[bench] " + "; ".join(f"{n} {r['us_per_step']} us" for n, r in others.items()),
               file=sys.stderr, flush=True)

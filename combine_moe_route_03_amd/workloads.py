@@ -52,12 +52,18 @@ WORKLOADS = {
                            "scale"),
     # Prefill batch: 4096 tokens, hidden 7168 bf16, 384 experts top-8, 48 ranks of 8 experts.
     "prefill": Workload("prefill", 4096, 7168, 384, 8, 48, "bf16", "bf16", "bf16", "bf16", "scale"),
+    # The prefill batch with block-scaled fp8-e4m3 dispatch and bf16 combine: the evaluation
+    # setting of the pages at 4096 tokens (same draws as "prefill").
+    "prefill_fp8": Workload("prefill_fp8", 4096, 7168, 384, 8, 48, "bf16", "fp8_e4m3", "bf16",
+                            "bf16", "scale"),
     # Skewed load: 8192 tokens, hidden 4096, 128 experts top-4, 16 ranks, Zipf(1.2) logit bias.
     "skewed": Workload("skewed", 8192, 4096, 128, 4, 16, "bf16", "bf16", "bf16", "bf16", "scale",
                        zipf_bias=True),
 }
 
 ORDER = ["tiny", "decode", "decode_fp8", "prefill", "skewed"]
+# Also checked at full size on the GPU: the pages' own prefill setting (fp8 dispatch).
+GPU_ORDER = ORDER + ["prefill_fp8"]
 
 
 @dataclass(frozen=True)

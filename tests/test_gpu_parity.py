@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from combine_moe_route_03_amd import _lib as moe
-from combine_moe_route_03_amd.workloads import ORDER, WORKLOADS, Workload, make_inputs, random_topk
+from combine_moe_route_03_amd.workloads import (GPU_ORDER, ORDER, WORKLOADS, Workload, make_inputs,
+                                                random_topk)
 from gpu_util import assert_close_out, to_dev, to_host
 
 pytestmark = [pytest.mark.gpu,
@@ -67,7 +68,7 @@ def test_route(name):
     _check_weights(to_host(g_w), wt)
 
 
-@pytest.mark.parametrize("name", ORDER)
+@pytest.mark.parametrize("name", GPU_ORDER)
 def test_dispatch(name):
     w = WORKLOADS[name]
     _announce(f"dispatch {name} T={w.T} H={w.H} E={w.E} k={w.k} N={w.N} payload={w.payload}")
@@ -80,7 +81,7 @@ def test_dispatch(name):
     _check_payload(buf, d, w.payload)
 
 
-@pytest.mark.parametrize("name", ORDER)
+@pytest.mark.parametrize("name", GPU_ORDER)
 def test_combine(name):
     w = WORKLOADS[name]
     _announce(f"combine {name} T={w.T} H={w.H} k={w.k} y={w.y_dtype} out={w.out_dtype}")
@@ -91,7 +92,7 @@ def test_combine(name):
     assert_close_out(to_host(res), out, w.out_dtype)
 
 
-@pytest.mark.parametrize("name", ORDER)
+@pytest.mark.parametrize("name", GPU_ORDER)
 def test_route_dispatch(name):
     """The fused entry point writes what the oracle's route and dispatch write."""
     w = WORKLOADS[name]
@@ -108,7 +109,7 @@ def test_route_dispatch(name):
     _check_payload(buf, d, w.payload)
 
 
-@pytest.mark.parametrize("name", ORDER)
+@pytest.mark.parametrize("name", GPU_ORDER)
 def test_full_chain_and_determinism(name):
     """Route -> dispatch -> combine on the GPU (its own weights and row maps) three times: separate
     route and dispatch calls, then the fused call twice on one reused, already written

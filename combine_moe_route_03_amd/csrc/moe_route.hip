@@ -2805,13 +2805,11 @@ moe_status_t route_dispatch(const float* logits, const void* x, moe_dtype_t x_dt
         launch_rows8(topk_idx, (int32_t)R, k, E, out->token_row, out->row_token,
                      count_outputs(out, n_ranks), ws, plan, wp, pf_rows, stream);
     } else {
-        // x is read ahead by the counting, scan and rows launches, a third each by default. The
-        // 16-lane routing-and-counting launch of many experts (E >= 256: 16 or more keys a lane)
-        // runs longest and takes half, scan and rows a quarter each. The wavefront-per-token
-        // routing launch (k > 16 or small batches) carries none, and scan and rows take halves.
-        const bool long_route = fused && !wide && E >= 256;
-        const int parts = wide ? 2 : (long_route ? 4 : 3);
-        const int q_route = wide ? 0 : (long_route ? 2 : 1);    // parts of each launch, in order
+        // x is read ahead by the counting, scan and rows launches, a third each; the
+        // wavefront-per-token routing launch (k > 16 or small batches) carries none, and scan and
+        // rows take halves.
+        const int parts = wide ? 2 : 3;
+        const int q_route = wide ? 0 : 1;                        // parts of each launch, in order
         const Prefetch pf_route = make_prefetch(x, x_bytes, ws, 0, parts, q_route);
         const Prefetch pf_scan = make_prefetch(x, x_bytes, ws, q_route, parts, 1);
         const Prefetch pf_rows = make_prefetch(x, x_bytes, ws, q_route + 1, parts, 1);

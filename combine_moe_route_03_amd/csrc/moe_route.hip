@@ -1790,12 +1790,25 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
 template <typename YT>
 struct Y8;
 
+// Loads of expert-output rows: non-temporal (NT, the default: rows read once, more of them than
+// the Infinity Cache holds), or plain, which lets a small batch's rows come from, and stay in, the
+// Infinity Cache (combine picks by the bytes it reads; see launch_combine_typed).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
 template <>
 struct Y8<uint16_t> {       // bf16: one 16-byte load per 8 elements
     u32x4 a;
+    template <bool NT = true>
     __device__ __forceinline__ void load(const uint16_t* p)
     {
-        a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        a = load16<NT>(reinterpret_cast<const u32x4*>(p));
     }
     __device__ __forceinline__ void fma_into(float w, float (&acc)[8]) const
     {
@@ -1811,10 +1824,11 @@ struct Y8<uint16_t> {       // bf16: one 16-byte load per 8 elements
 template <>
 struct Y8<float> {          // fp32: two 16-byte loads per 8 elements
     u32x4 a, b;
+    template <bool NT = true>
     __device__ __forceinline__ void load(const float* p)
     {
-        a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-        b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
+        a = load16<NT>(reinterpret_cast<const u32x4*>(p));
+        b = load16<NT>(reinterpret_cast<const u32x4*>(p) + 1);
     }
     __device__ __forceinline__ void fma_into(float w, float (&acc)[8]) const
     {
@@ -1857,8 +1871,8 @@ struct Store8<float> {
 
 // One wavefront per (token, segment of 64 chunks = 512 elements); lane l owns chunk
 // segment*64 + l. KC is k when it is a compile-time constant (all k loads issued before the
-// first multiply-add), else 0.
-template <typename YT, typename OT, int KC>
+// first multiply-add), else 0; NT selects non-temporal row loads (Y8::load).
+template <typename YT, typename OT, int KC, bool NT>
 __global__ __launch_bounds__(64 * kCombineWaves) void k_combine(
     const YT* __restrict__ y, int32_t T, int32_t H, int32_t k_rt, int32_t R, int32_t nseg,
     const int32_t* __restrict__ token_row, const float* __restrict__ topk_w,
@@ -1886,7 +1900,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_combine(
             const int row = token_row[t * KC + j];
             w[j] = topk_w[t * KC + j];
             if ((uint32_t)row < (uint32_t)R) {
-                v[j].load(y + (int64_t)row * H + off);
+                v[j].template load<NT>(y + (int64_t)row * H + off);
             } else {
                 w[j] = 0.0f;
                 v[j] = Y8<YT>{};
@@ -1901,7 +1915,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_combine(
             if ((uint32_t)row >= (uint32_t)R)
                 continue;
             Y8<YT> v;
-            v.load(y + (int64_t)row * H + off);
+            v.template load<NT>(y + (int64_t)row * H + off);
             v.fma_into(topk_w[t * k + j], acc);
         }
     }
@@ -2611,6 +2625,14 @@ void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H
         k_layout_pack<LP_FP8_BF16, 0><<<grid, kLpThreads, lds, stream>>>(lp, co);
 }
 
+// Rows read by combine up to this many bytes are loaded plainly (they fit the 256 MB Infinity
+// Cache many times over, and a small batch's rows were just written): measured at hidden 7168,
+// 256 experts, top-8, the decode step takes 15.3 us with plain loads against 17.2 us with
+// non-temporal ones, and 256 tokens (29 MB of rows) 21.4 against 22.1 us; from 512 tokens (59 MB)
+// on, non-temporal loads win (34.3 against 35.6 us; the 4096-token prefill step 186.9 against
+// 192.2 us).
+constexpr int64_t kCombinePlainLoadBytes = 32ll << 20;
+
 template <typename YT, typename OT>
 void launch_combine_typed(const void* y, int32_t T, int32_t H, int32_t k,
                           const int32_t* token_row, const float* topk_w, void* out, int32_t R,
@@ -2620,9 +2642,16 @@ void launch_combine_typed(const void* y, int32_t T, int32_t H, int32_t k,
     const dim3 grid((unsigned)ceil_div((int64_t)T * nseg, kCombineWaves));
     const YT* yp = static_cast<const YT*>(y);
     OT* op = static_cast<OT*>(out);
+    const bool nt = (int64_t)T * k * H * (int64_t)sizeof(YT) > kCombinePlainLoadBytes;
 #define MOE_COMBINE(KK)                                                                           \
-    k_combine<YT, OT, KK><<<grid, 64 * kCombineWaves, 0, stream>>>(yp, T, H, k, R, nseg,         \
-                                                                   token_row, topk_w, op)
+    do {                                                                                          \
+        if (nt)                                                                                   \
+            k_combine<YT, OT, KK, true><<<grid, 64 * kCombineWaves, 0, stream>>>(                 \
+                yp, T, H, k, R, nseg, token_row, topk_w, op);                                     \
+        else                                                                                      \
+            k_combine<YT, OT, KK, false><<<grid, 64 * kCombineWaves, 0, stream>>>(                \
+                yp, T, H, k, R, nseg, token_row, topk_w, op);                                     \
+    } while (0)
     switch (k) {
     case 1: MOE_COMBINE(1); break;
     case 2: MOE_COMBINE(2); break;

@@ -47,6 +47,10 @@ def parse_args():
     p.add_argument("--settle-seconds", type=float, default=0.3,
                    help="before the warmup steps, run the plain copy kernel this long so the GPU "
                         "reaches its steady clocks (0 disables it)")
+    p.add_argument("--settle-step-seconds", type=float, default=0.04,
+                   help="after the copy kernel, run the step itself this long (untimed) before "
+                        "the warmup steps, so the timed steps start at the GPU's steady state "
+                        "under this workload (0 disables it)")
     p.add_argument("--sets", type=int, default=8,
                    help="buffer sets used in rotation (each set is about 1 GB at prefill). With "
                         "2 sets the activations and logits of a set (65 MB at prefill) are still "
@@ -192,6 +196,31 @@ def settle_clocks(torch, seconds: float) -> float:
     return time.perf_counter() - t0
 
 
+def settle_steps(torch, sets, phases, seconds: float) -> int:
+    """After settle_clocks, run the step itself back to back over the buffer sets for about
+    `seconds` (untimed), keeping the launch queue fed: the host waits only for the chunk before
+    the last. Measured at prefill (8 sets, blocks of 20 steps after the copy kernel): the step
+    takes 190, 190, 187, 186 us in the first four blocks and 185 us from about step 100 on; after
+    150 steps of this settle the first block is already at 185 us. Without the copy kernel first,
+    150 steps are not enough (195, 201, 193 us). Returns the number of steps run."""
+    if seconds <= 0:
+        return 0
+    chunk, pending, n = 16, [], 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(chunk):
+            for ph in phases:
+                sets[n % len(sets)][ph]()
+            n += 1
+        ev = torch.cuda.Event()
+        ev.record()
+        pending.append(ev)
+        if len(pending) > 1:
+            pending.pop(0).synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def hbm_traffic(kernel_pattern: str):
     """Counter-measured HBM bytes per launch of the kernel whose name (template arguments
     included) matches `kernel_pattern`, from the committed profile: (name, bytes), or
@@ -307,15 +336,17 @@ def timed(torch, sets, phases, K, per_call_events):
 HEADLINE = ("route_dispatch", "combine")
 
 
-def other_workloads(torch, moe, dev, names, K, n_sets):
+def other_workloads(torch, moe, dev, names, K, n_sets, settle_s, settle_step_s):
     """The headline step on the smaller workloads (latency-bound ones are reported in us), over
-    n_sets buffer sets in rotation."""
+    n_sets buffer sets in rotation, each after the same settle as the headline workload."""
     from combine_moe_route_03_amd.workloads import WORKLOADS, make_inputs
     res = {}
     for name in names:
         w = WORKLOADS[name]
         inp = make_inputs(w)
         sets = [make_set(w, inp, dev, moe, torch) for _ in range(n_sets)]
+        settle_clocks(torch, settle_s)
+        settle_steps(torch, sets, HEADLINE, settle_step_s)
         for i in range(10):
             for ph in HEADLINE:
                 sets[i % n_sets][ph]()
@@ -511,6 +542,7 @@ def main():
     separate = ("route", "dispatch", "combine")
     split = ("route", "layout", "pack", "combine")
     settled_s = settle_clocks(torch, args.settle_seconds)
+    n_settle = settle_steps(torch, sets, headline, args.settle_step_seconds)
     for i in range(args.warmup):
         for ph in headline:
             sets[i % len(sets)][ph]()
@@ -557,7 +589,8 @@ def main():
         print("[bench] other workloads", file=sys.stderr, flush=True)
         others = other_workloads(torch, moe, dev,
                                  ("tiny", "decode", "decode_fp8", "skewed", "prefill_fp8"),
-                                 100, max(1, args.sets))
+                                 100, max(1, args.sets), args.settle_seconds,
+                                 args.settle_step_seconds)
         print("[bench] " + "; ".join(f"{n} {r['us_per_step']} us" for n, r in others.items()),
               file=sys.stderr, flush=True)
         ep = ep_emulation(torch, moe, dev, 20)
@@ -615,6 +648,7 @@ def main():
         "ep_emulation": ep,
         "wall_s_timed_loop": round(wall, 4),
         "clock_settle_s": round(settled_s, 3),
+        "settle_steps": n_settle,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -406,6 +406,7 @@ struct Prefetch {
     const u32x4* x;       // first chunk to read (null: no prefetch)
     int64_t chunks;       // 16-byte chunks to read
     int32_t groups;       // workgroups that share them
+    int32_t sleeps;       // s_sleep(16) (1024 shader clocks) before the first load, this many
     uint32_t* sink;       // a workspace word that nothing reads
 };
 
@@ -413,9 +414,12 @@ constexpr int kPrefetchChunksPerThread = 16;
 constexpr int64_t kPrefetchMaxBytes = 128ll << 20;   // half the Infinity Cache
 
 // Workgroup g of pf.groups reads its contiguous span of the chunks, four loads in flight per
-// thread. The loaded words feed one data-dependent store to pf.sink, which keeps the loads.
+// thread, after pf.sleeps sleeps of about half a microsecond. The loaded words feed one
+// data-dependent store to pf.sink, which keeps the loads.
 __device__ __forceinline__ void prefetch_span(const Prefetch& pf, int g)
 {
+    for (int z = 0; z < pf.sleeps; ++z)
+        __builtin_amdgcn_s_sleep(16);
     const int64_t per = (pf.chunks + pf.groups - 1) / pf.groups;
     const int64_t b = (int64_t)g * per;
     const int64_t e = b + per < pf.chunks ? b + per : pf.chunks;
@@ -2318,15 +2322,16 @@ inline Prefetch no_prefetch()
     pf.x = nullptr;
     pf.chunks = 0;
     pf.groups = 0;
+    pf.sleeps = 0;
     pf.sink = nullptr;
     return pf;
 }
 
 // Parts [part, part + n) of `parts` equal parts of the x prefetch: the first kPrefetchMaxBytes of
-// x at most (the first windows pack first), in 16-byte chunks, 16 chunks a thread. x null, or a
-// range outside [0, parts): none.
+// x at most (the first windows pack first), in 16-byte chunks, 16 chunks a thread, after `sleeps`
+// sleeps. x null, or a range outside [0, parts): none.
 Prefetch make_prefetch(const void* x, int64_t x_bytes, const Workspace& ws, int part, int parts,
-                       int n = 1)
+                       int n = 1, int sleeps = 0)
 {
     if (part < 0 || n < 1 || part + n > parts)
         return no_prefetch();
@@ -2337,6 +2342,7 @@ Prefetch make_prefetch(const void* x, int64_t x_bytes, const Workspace& ws, int 
     pf.x = static_cast<const u32x4*>(x) + b;
     pf.chunks = e - b;
     pf.groups = (int32_t)ceil_div(pf.chunks, (int64_t)kThreads * kPrefetchChunksPerThread);
+    pf.sleeps = sleeps;
     pf.sink = ws.sink;
     return pf;
 }
@@ -2826,8 +2832,12 @@ moe_status_t route_dispatch(const float* logits, const void* x, moe_dtype_t x_dt
     if (fused && rows8_fits(plan, wp, E)) {
         // two layout launches: routing with counting (byte counts), then the rows, each reading
         // half of x ahead; the wavefront-per-token routing launch carries none, and the rows
-        // launch reads all of it
-        const Prefetch pf_route = wide ? no_prefetch() : make_prefetch(x, x_bytes, ws, 0, 2);
+        // launch reads all of it. The routing launch's read-ahead starts about 1 us late, so the
+        // routing workgroups' logit loads go first: measured at prefill (200 steps, 3 runs, one
+        // box) 183.8-183.9 us per step against 184.8-185.5 with no sleep; 1, 3, 4 and 6 sleeps
+        // gave 184.8-184.9, 183.7-184.0, 184.3-184.5 and 185.3; a sleep in the rows launch's
+        // read-ahead costs (186.8-187.2 with 2).
+        const Prefetch pf_route = wide ? no_prefetch() : make_prefetch(x, x_bytes, ws, 0, 2, 1, 2);
         const Prefetch pf_rows = wide ? make_prefetch(x, x_bytes, ws, 0, 1)
                                       : make_prefetch(x, x_bytes, ws, 1, 2);
         launch_route_layout(logits, T, E, k, topk_idx, topk_w, ws, plan, pf_route, true, stream);

@@ -1485,24 +1485,76 @@ struct Load8<uint16_t> {
     }
 };
 
+// Four e4m3 codes of quotients d with |d| < 464 or NaN, by the hardware conversion (round to
+// nearest even; byte i of the result is the code of d[i]). The magnitude bits are kept and the sign
+// is taken from d: for every such fp32 pattern this equals f32_to_e4m3 (checked over all 2^32
+// patterns on gfx950; the hardware gives NaN one fixed sign, f32_to_e4m3 keeps the input's).
+__device__ __forceinline__ uint32_t e4m3x4_hw(float d0, float d1, float d2, float d3)
+{
+    uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(d2, d3, c, true);
+    const uint32_t sign = ((__float_as_uint(d0) >> 31) << 7) | ((__float_as_uint(d1) >> 31) << 15) |
+                          ((__float_as_uint(d2) >> 31) << 23) | (__float_as_uint(d3) & 0x80000000u);
+    return (c & 0x7F7F7F7Fu) | sign;
+}
+
 // Block-scaled e4m3 of the 8 elements a lane holds, the 16 lanes of each DPP row forming one
 // 128-element block (every lane of the wavefront takes part in the row maximum): scale
-// s = amax / 448 (1 for an all-zero block, the division correctly rounded), codes e4m3(v / s),
-// packed little-endian into 8 bytes. Returns s.
+// s = amax / 448 (1 for an all-zero block, the division correctly rounded), codes e4m3(v / s) with
+// v / s the correctly rounded fp32 quotient, packed little-endian into 8 bytes. Returns s.
+//   - Usual blocks (amax finite, s normal, amax < 2^127): the quotient comes from the correctly
+//     rounded reciprocal r = 1/s, q0 = |v|*r and one fused correction q0 + (|v| - q0*s)*r
+//     (Markstein's division theorem: with r correctly rounded and q0 within an ulp, the corrected
+//     quotient is the correctly rounded one, as long as the residual |v| - q0*s is exact). The
+//     residual is formed on |v| and s scaled by 2^(127 - exponent of amax), exactly, so it cannot
+//     underflow where the code is not zero; below 2^-11 the quotient may differ in its last bits but
+//     both round to a zero code. The sign is copied from v. The codes then come from the hardware
+//     conversion. Checked on gfx950 for every pair of bf16 values (v, amax) with |v| <= amax: the
+//     codes equal those of the correctly rounded division and f32_to_e4m3.
+//   - An all-zero block: s = 1, the quotient is v itself.
+//   - Otherwise (amax infinite, s below the normal range, amax >= 2^127) the correctly rounded
+//     division and f32_to_e4m3, which also saturate the infinite quotients these blocks can give.
+// The case is the same for the 16 lanes of a row.
 __device__ __forceinline__ float quantise8_e4m3(const float (&v)[8], u32x2& packed)
 {
+    // NaN elements, signalling ones too, take no part in the maximum: a comparison skips them,
+    // where fmaxf would return NaN for a signalling NaN operand
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        amax = fmaxf(amax, fabsf(v[i]));
+    for (int i = 0; i < 8; ++i) {
+        const float a = fabsf(v[i]);
+        amax = a > amax ? a : amax;
+    }
     amax = max_row16_f32(amax);
     const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-    uint32_t q[8];
+    const uint32_t ea = __float_as_uint(amax) >> 23;    // amax >= +0, never NaN
+    float d[8];
+    if (amax == 0.0f) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        q[i] = f32_to_e4m3(v[i] / s);
-    packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-    packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        for (int i = 0; i < 8; ++i)
+            d[i] = v[i];
+    } else if (ea <= 253u && s >= 0x1p-126f) {
+        const float r = 1.0f / s;
+        const float up = __uint_as_float((254u - ea) << 23);     // 2^(127 - ea)
+        const float down = __uint_as_float(ea << 23);            // 2^(ea - 127)
+        const float s_up = s * up, r_down = r * down;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float a = fabsf(v[i]);
+            const float q0 = a * r;
+            d[i] = copysignf(fmaf(fmaf(-q0, s_up, a * up), r_down, q0), v[i]);
+        }
+    } else {
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            q[i] = f32_to_e4m3(v[i] / s);
+        packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        return s;
+    }
+    packed.x = e4m3x4_hw(d[0], d[1], d[2], d[3]);
+    packed.y = e4m3x4_hw(d[4], d[5], d[6], d[7]);
     return s;
 }
 

@@ -339,6 +339,56 @@ def test_fp8_special_blocks():
         _check_payload(buf, d, "fp8_e4m3")
 
 
+def _quantiser_sweep_x(x_dtype: str, T_min: int, H: int = 4096) -> np.ndarray:
+    """Blocks of 128 that pair every bf16 value (NaN included, infinities excluded) with a set of
+    block maxima: each block holds one maximum A (either sign) and 127 values of magnitude at most
+    |A|, at shuffled positions. The maxima reach every case of the quantiser: s subnormal, s at the
+    bottom of the normal range, ordinary scales, amax of 2^126 and above 2^127. For f32 x, blocks of
+    random full-precision values at each maximum are added. Rows past the blocks are N(0, 1)."""
+    rng = np.random.default_rng(11)
+    vals = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    vals = vals[~np.isinf(vals)]
+    maxima = np.array([2.0 ** -133, 2.0 ** -126, 1e-36, 5.3e-36, 1e-30, 2.0 ** -117, 1e-5, 0.37,
+                       1.0, 3.0, 448.0, 1e4, 2.0 ** 126, 3.0e38], np.float32)
+    maxima = (oracle.f32_to_bf16(maxima).astype(np.uint32) << 16).view(np.float32)
+    blocks = []
+    for a in maxima:
+        sel = vals[np.isnan(vals) | (np.abs(vals) <= a)].copy()
+        rng.shuffle(sel)
+        nb = -(-sel.size // 127)
+        sel = np.concatenate([sel, np.zeros(nb * 127 - sel.size, np.float32)]).reshape(nb, 127)
+        if x_dtype == "f32":
+            rnd = (rng.uniform(-1.0, 1.0, (64, 127)) * a).astype(np.float32)
+            sel = np.concatenate([sel, rnd])
+        first = np.where(rng.random(sel.shape[0]) < 0.5, -a, a).astype(np.float32)
+        blocks.append(rng.permuted(np.concatenate([first[:, None], sel], 1), axis=1))
+    b = np.concatenate(blocks)
+    per_row = H // 128
+    rows = -(-b.shape[0] // per_row)
+    b = np.concatenate([b, np.zeros((rows * per_row - b.shape[0], 128), np.float32)])
+    x = b.reshape(rows, H)
+    if rows < T_min:
+        x = np.concatenate([x, rng.standard_normal((T_min - rows, H)).astype(np.float32)])
+    return x if x_dtype == "f32" else oracle.f32_to_bf16(x)
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T_min", [0, 700])
+def test_fp8_quantiser_sweep(x_dtype, T_min):
+    """Every bf16 value against block maxima from the subnormal to the largest range, through the
+    one-launch (T <= 512) and the multi-launch packing; codes and scales bit-exact."""
+    x = _quantiser_sweep_x(x_dtype, T_min)
+    T, H, E, k, N = x.shape[0], x.shape[1], 2, 1, 2
+    _announce(f"edge fp8 quantiser sweep x={x_dtype} T={T} H={H}")
+    idx = (np.arange(T, dtype=np.int32) % E).reshape(T, 1)
+    d = oracle.dispatch(x, x_dtype, idx, E, N, "fp8_e4m3")
+    buf = moe.alloc_dispatch_out(T, H, E, k, N, "fp8_e4m3")
+    moe.moe_dispatch(to_dev(x, x_dtype), to_dev(idx, "i32"), E, N, buf,
+                     moe.alloc_workspace(T, E, k))
+    torch.cuda.synchronize()
+    _check_payload(buf, d, "fp8_e4m3")
+
+
 def test_zero_tokens_writes_zero_counts():
     E, N, k = 16, 4, 2
     _announce("edge T=0")

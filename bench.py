@@ -479,6 +479,7 @@ def ep_emulation(torch, moe, dev, K):
         torch.cuda.synchronize()
         for p, ph in enumerate(rorder):
             rtot[ph] += e[p].elapsed_time(e[p + 1])
+    overlap = send_overlap(torch, calls["send"], S * T, H, dev, K)
     full_o = torch.cat(out).view(torch.int16).to(torch.int32)
     red_o = torch.cat(out_red).view(torch.int16).to(torch.int32)
     mono = lambda v: torch.where(v < 0, -(v & 0x7FFF), v)  # noqa: E731
@@ -506,7 +507,55 @@ def ep_emulation(torch, moe, dev, K):
                 "bytes_saved_frac": round(1 - rows_back / rows_total, 4),
                 "vs_receiver_only_max_bf16_codes": int(dist.max().item()),
                 "vs_receiver_only_frac_elements_differing": round(
-                    float((dist > 0).float().mean().item()), 5)}}
+                    float((dist > 0).float().mean().item()), 5)},
+            "send_overlap": overlap}
+
+
+def send_overlap(torch, sends, tokens, H, dev, K, inter=2048):
+    """What the sender half leaves free: the S sends (main stream) beside a dense bf16 matmul of the
+    same tokens on a second stream (default priority), standing in for a shared expert's first
+    projection [tokens, H] x [H, inter]. Times each alone and both together, forked and joined by
+    events; `hidden_us` is how much of the shorter one the overlap hides."""
+    a = torch.randn((tokens, H), device=dev).to(torch.bfloat16)
+    b = torch.randn((H, inter), device=dev).to(torch.bfloat16)
+    c = torch.empty((tokens, inter), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def run_sends():
+        for f in sends:
+            f()
+
+    def run_mm():
+        with torch.cuda.stream(side):
+            torch.matmul(a, b, out=c)
+
+    def timed_loop(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fork = torch.cuda.Event()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            fork.record(main)
+            side.wait_event(fork)
+            fn()
+            main.wait_stream(side)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3
+
+    for fn in (run_sends, run_mm):
+        fn()
+    torch.cuda.synchronize()
+    t_send = timed_loop(run_sends)
+    t_mm = timed_loop(run_mm)
+    t_both = timed_loop(lambda: (run_mm(), run_sends()))
+    flops = 2.0 * tokens * H * inter
+    return {"sends_us": round(t_send, 1), "matmul_us": round(t_mm, 1),
+            "matmul": f"[{tokens}, {H}] x [{H}, {inter}] bf16, {flops / (t_mm * 1e-6) / 1e12:.0f} "
+                      f"TFLOP/s alone",
+            "together_us": round(t_both, 1),
+            "hidden_us": round(t_send + t_mm - t_both, 1)}
 
 
 def main():
@@ -596,7 +645,8 @@ def main():
         ep = ep_emulation(torch, moe, dev, 20)
         torch.cuda.empty_cache()
         print(f"[bench] expert-parallel emulation: step {ep['step_us']} us, "
-              f"per call {ep['per_call_us']}", file=sys.stderr, flush=True)
+              f"per call {ep['per_call_us']}; sends beside a matmul {ep['send_overlap']}",
+              file=sys.stderr, flush=True)
 
     cpu = None
     if args.cpu_seconds > 0:

@@ -11,6 +11,10 @@
 //    q = q0 + (|v|*2^j - q0*(s*2^j)) * (r*2^-j) with 2^j = 2^(127 - exponent of amax), sign of v;
 //    its code against the code of the correctly rounded fp32 quotient v/s, for every pair of bf16
 //    values (v, amax) with |v| <= amax, amax finite and not 0, s = amax/448 normal, amax < 2^127.
+// 3. The same comparison for 2^32 pseudo-random fp32 pairs (v, amax) of the fast path (full 24-bit
+//    significands, amax over the whole range that gives a normal s, v from the same binade as amax
+//    down to 40 binades below it and into the subnormals), drawn from a counter-based hash of the
+//    pair's index (splitmix64's finaliser).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,12 +61,21 @@ __device__ float fast_quotient(float v, float s, float amax)
     return copysignf(fmaf(fmaf(-q0, s * up, a * up), r * down, q0), v);
 }
 
-// counts: [0] encoder inputs, [1] encoder mismatches, [2] quotient pairs, [3] code mismatches
+__device__ uint64_t mix64(uint64_t z)
+{
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// counts: [0] encoder inputs, [1] encoder mismatches, [2] bf16 quotient pairs, [3] their code
+// mismatches, [4] random fp32 pairs, [5] their code mismatches
 __global__ void k_check(unsigned long long* counts)
 {
     const uint64_t n = 1ull << 32;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    unsigned long long c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    unsigned long long c0 = 0, c1 = 0, c2 = 0, c3 = 0, c4 = 0, c5 = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const uint32_t u = (uint32_t)i;
         const float d = __uint_as_float(u);
@@ -79,6 +92,20 @@ __global__ void k_check(unsigned long long* counts)
                 c3 += e4m3_hw(fast_quotient(v, s, amax)) != e4m3_def(v / s) ? 1u : 0u;
             }
         }
+        const uint64_t z = mix64(i);
+        const uint32_t ea = 10u + (uint32_t)(z % 243u);                     // amax in [2^-117, 2^126)
+        const float ra = __uint_as_float((ea << 23) | (uint32_t)((z >> 8) & 0x7FFFFFu));
+        const uint32_t drop = (uint32_t)((z >> 32) % 41u);
+        const uint32_t ev = ea > drop ? ea - drop : 0u;                      // 0: a subnormal v
+        float rv = __uint_as_float(((uint32_t)(z >> 63) << 31) | (ev << 23) |
+                                   (uint32_t)((z >> 36) & 0x7FFFFFu));
+        if (fabsf(rv) > ra)
+            rv = copysignf(ra, rv);
+        const float rs = ra / 448.0f;
+        if (rs >= 0x1p-126f) {
+            ++c4;
+            c5 += e4m3_hw(fast_quotient(rv, rs, ra)) != e4m3_def(rv / rs) ? 1u : 0u;
+        }
     }
     // one atomic per wavefront and counter
     for (int off = 32; off > 0; off >>= 1) {
@@ -86,26 +113,30 @@ __global__ void k_check(unsigned long long* counts)
         c1 += __shfl_down(c1, off, 64);
         c2 += __shfl_down(c2, off, 64);
         c3 += __shfl_down(c3, off, 64);
+        c4 += __shfl_down(c4, off, 64);
+        c5 += __shfl_down(c5, off, 64);
     }
     if ((threadIdx.x & 63) == 0) {
         atomicAdd(&counts[0], c0);
         atomicAdd(&counts[1], c1);
         atomicAdd(&counts[2], c2);
         atomicAdd(&counts[3], c3);
+        atomicAdd(&counts[4], c4);
+        atomicAdd(&counts[5], c5);
     }
 }
 
 }  // namespace
 
-// Runs both checks on the current device; writes the four counts to host memory. Returns 0, or
-// the HIP error code.
+// Runs the three checks on the current device; writes the six counts to host memory. Returns 0,
+// or the HIP error code.
 extern "C" int e4m3_hw_check(unsigned long long* host_counts)
 {
     unsigned long long* d = nullptr;
-    hipError_t err = hipMalloc(&d, 4 * sizeof(unsigned long long));
+    hipError_t err = hipMalloc(&d, 6 * sizeof(unsigned long long));
     if (err != hipSuccess)
         return (int)err;
-    err = hipMemset(d, 0, 4 * sizeof(unsigned long long));
+    err = hipMemset(d, 0, 6 * sizeof(unsigned long long));
     if (err == hipSuccess) {
         k_check<<<16384, 256>>>(d);
         err = hipGetLastError();
@@ -113,7 +144,7 @@ extern "C" int e4m3_hw_check(unsigned long long* host_counts)
     if (err == hipSuccess)
         err = hipDeviceSynchronize();
     if (err == hipSuccess)
-        err = hipMemcpy(host_counts, d, 4 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+        err = hipMemcpy(host_counts, d, 6 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
     const hipError_t err2 = hipFree(d);
     return (int)(err != hipSuccess ? err : err2);
 }

@@ -411,7 +411,11 @@ struct Prefetch {
 };
 
 constexpr int kPrefetchChunksPerThread = 16;
-constexpr int64_t kPrefetchMaxBytes = 128ll << 20;   // half the Infinity Cache
+// At most 7/8 of the 256 MB Infinity Cache is read ahead. Measured, µs per step (hidden 7168,
+// 8 buffer sets): 16384 tokens, E 256 (235 MB of x) 778.9 with a 128 MiB cap, 766-767 (160 MiB),
+// 752-753 (192), 741 (224), 742 (256); 12288 tokens, E 384 (176 MB) 602 (128), 597 (160), 585-587
+// from 192 MiB on.
+constexpr int64_t kPrefetchMaxBytes = 224ll << 20;
 
 // Workgroup g of pf.groups reads its contiguous span of the chunks, four loads in flight per
 // thread, after pf.sleeps sleeps of about half a microsecond. The loaded words feed one

@@ -66,6 +66,8 @@ constexpr int kLpTokens = 512;           // layout folded into packing: at most 
 constexpr int kLpThreads = 512;          //   (8 wavefronts a workgroup, two experts a thread)
 constexpr int kLpWaves = kLpThreads / 64;
 constexpr int kLpMaxGroups = 1024;       //   (grid-stride beyond this many workgroups)
+constexpr int kLpWideThreads = 1024;     //   above kLpWideTokens tokens, 16 wavefronts a
+constexpr int kLpWideTokens = 256;       //   workgroup (row copies without routing)
 constexpr int kLpRouteTokens = kLpThreads / 16;   // routing in the same launch: at most 32 tokens
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -1673,11 +1675,11 @@ __device__ __forceinline__ void lp_load(const LayoutPackPlan& lp, int64_t t, int
         Load8<float>::run(static_cast<const float*>(lp.x) + t * lp.H + c * 8, v);
 }
 
-template <int MODE, int RP>
-__global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, CountOutputs co)
+template <int MODE, int RP, int NT = kLpThreads>
+__global__ __launch_bounds__(NT) void k_layout_pack(LayoutPackPlan lp, CountOutputs co)
 {
     extern __shared__ uint32_t lds_lp[];
-    __shared__ uint32_t wave_tot[kLpWaves];
+    __shared__ uint32_t wave_tot[NT / 64];
     __shared__ uint32_t repeated;
     const int32_t E = lp.E, W = lp.words, k = lp.k;
     uint32_t* mask = lds_lp;                             // [W][E]
@@ -1685,9 +1687,9 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
     int32_t* ids = reinterpret_cast<int32_t*>(eoff + E + 1);     // [T * k] when routing here
     const int32_t* __restrict__ topk_idx = RP > 0 ? ids : lp.topk_idx;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t waves = (int64_t)gridDim.x * kLpWaves;
+    const int64_t waves = (int64_t)gridDim.x * (NT / 64);
     const int64_t units = (int64_t)lp.T * lp.pieces;
-    int64_t u = (int64_t)blockIdx.x * kLpWaves + (tid >> 6);       // uniform per wavefront
+    int64_t u = (int64_t)blockIdx.x * (NT / 64) + (tid >> 6);       // uniform per wavefront
 
     // the first unit's payload and ids, in flight while the layout is built
     u32x4 xv = {0u, 0u, 0u, 0u};
@@ -1706,9 +1708,9 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
     }
 
     // routing (RP > 0, k <= 16): every workgroup routes the whole batch into LDS, 16 lanes a
-    // token, kLpThreads / 16 tokens a pass; workgroup 0 also writes the ids and weights
+    // token, NT / 16 tokens a pass; workgroup 0 also writes the ids and weights
     if constexpr (RP > 0) {
-        for (int q0 = 0; q0 < lp.T; q0 += kLpThreads / 16) {     // uniform across the workgroup
+        for (int q0 = 0; q0 < lp.T; q0 += NT / 16) {     // uniform across the workgroup
             const int q = q0 + (tid >> 4);
             const bool valid = q < lp.T;
             float lg[RP];
@@ -1725,15 +1727,15 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
     }
 
     // the layout, in every workgroup
-    for (int i = tid; i < W * E; i += kLpThreads)
+    for (int i = tid; i < W * E; i += NT)
         mask[i] = 0u;
-    for (int i = tid; i <= E; i += kLpThreads)
+    for (int i = tid; i <= E; i += NT)
         eoff[i] = 0u;
     if (tid == 0)
         repeated = 0u;
     __syncthreads();
     const int32_t R = lp.T * k;
-    for (int32_t i = tid; i < R; i += kLpThreads) {
+    for (int32_t i = tid; i < R; i += NT) {
         const int32_t e = topk_idx[i];
         if ((uint32_t)e < (uint32_t)E) {
             const int32_t tt = i / k;
@@ -1744,11 +1746,11 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
         }
     }
     __syncthreads();
-    const int e0 = 2 * tid, e1 = 2 * tid + 1;            // E <= 2 * kLpThreads
+    const int e0 = 2 * tid, e1 = 2 * tid + 1;            // E <= 2 * NT
     const uint32_t c0 = e0 < E ? eoff[e0] : 0u;
     const uint32_t c1 = e1 < E ? eoff[e1] : 0u;
     uint32_t total = 0u;
-    const uint32_t ex = block_exclusive_scan<kLpThreads>(c0 + c1, wave_tot, &total);
+    const uint32_t ex = block_exclusive_scan<NT>(c0 + c1, wave_tot, &total);
     if (e0 < E)
         eoff[e0] = ex;
     if (e1 < E)
@@ -1758,16 +1760,16 @@ __global__ __launch_bounds__(kLpThreads) void k_layout_pack(LayoutPackPlan lp, C
     __syncthreads();
     const bool exact = repeated != 0u;                   // uniform over the grid
     if (blockIdx.x == 0 && lp.ep_L > 0) {
-        for (int e = tid; e < E; e += kLpThreads)
+        for (int e = tid; e < E; e += NT)
             lp.ep_counts[((int64_t)(e / lp.ep_L) * lp.ep_sources + lp.ep_source) * lp.ep_L +
                          e % lp.ep_L] = (int32_t)(eoff[e + 1] - eoff[e]);
     } else if (blockIdx.x == 0) {
         const int epr = E / co.N;
-        for (int e = tid; e < E; e += kLpThreads) {
+        for (int e = tid; e < E; e += NT) {
             co.expert_offsets[e] = (int32_t)eoff[e];
             co.expert_counts[e] = (int32_t)(eoff[e + 1] - eoff[e]);
         }
-        for (int r = tid; r < co.N; r += kLpThreads) {
+        for (int r = tid; r < co.N; r += NT) {
             co.rank_offsets[r] = (int32_t)eoff[r * epr];
             co.rank_counts[r] = (int32_t)(eoff[(r + 1) * epr] - eoff[r * epr]);
         }
@@ -2684,6 +2686,17 @@ void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H
         return;
     }
     const size_t lds = lp_lds_bytes(T, E);
+    if (T > kLpWideTokens && !layout_only && !fp8) {
+        // 16 wavefronts a workgroup: half the workgroups, so half the layouts rebuilt. Measured
+        // at hidden 7168 bf16, E 256, k 8 (µs per step): 384 tokens 27.05 -> 26.7, 512 tokens
+        // 34.2 -> 32.6, 256 and fewer unchanged or slower. The fp8 modes keep 8 wavefronts: their
+        // quantising workgroups ran 24.2 -> 28.0 us at 384 tokens (fewer, longer workgroups than
+        // CUs can take in one round).
+        const int64_t groups16 = ceil_div((int64_t)T * lp.pieces, kLpWideThreads / 64);
+        const dim3 grid16((unsigned)(groups16 < kLpMaxGroups ? groups16 : kLpMaxGroups));
+        k_layout_pack<LP_COPY, 0, kLpWideThreads><<<grid16, kLpWideThreads, lds, stream>>>(lp, co);
+        return;
+    }
     if (layout_only)
         k_layout_pack<LP_LAYOUT, 0><<<grid, kLpThreads, lds, stream>>>(lp, co);
     else if (!fp8)

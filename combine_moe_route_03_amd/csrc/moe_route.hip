@@ -76,12 +76,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------- number formats --
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// bf16 nearest to f, ties to even (add half an ulp minus one, plus the kept lsb, then truncate).
+// bf16 nearest to f, ties to even (add half an ulp minus one, plus the kept lsb, then truncate);
+// every NaN becomes the one quiet NaN 0x7FC0 (its sign and payload are not kept).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return ((u >> 16) | 0x40u) & 0xFFFFu;           // NaN stays a quiet NaN
+        return 0x7FC0u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 

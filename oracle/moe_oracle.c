@@ -225,8 +225,10 @@ int oracle_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* 
  *   in token order (the grouped-GEMM input the receiver fills in "Dispatch en Combine");
  *   payload: row token_row[t*k+j] holds token t, as the same bytes for f32/bf16, or as block-scaled
  *   fp8 (reading of "block-scaled fp8-dispatch": per token and per block of 128 consecutive
- *   elements, amax = max |x|, scale s = amax/448 in fp32, or 1 if amax = 0, code = e4m3(x/s)
- *   rounded to nearest even and saturated at 448; all fp32 operations, as on the GPU).
+ *   elements, amax = max |x| over the elements that are not NaN, scale s = amax/448 in fp32, or 1
+ *   if amax = 0, code = e4m3(x/s) rounded to nearest even and saturated at 448; all fp32
+ *   operations, as on the GPU. s is positive, so every quotient has the sign of x; IEEE 754 leaves
+ *   the sign of a NaN result open (an infinite x over an infinite s), and it is taken as x's too).
  * Expert ids must lie in [0, E); a repeated id in one token is two separate items.
  * ---------------------------------------------------------------------------------------------- */
 typedef struct {
@@ -325,7 +327,7 @@ int oracle_dispatch(const void* x, int32_t x_dtype, int32_t T, int32_t H, const 
             s[b] = (amax == 0.0f) ? 1.0f : amax / 448.0f;
             for (int h = b * 128; h < (b + 1) * 128; h++) {
                 float xv = (float)load_elem(x, x_dtype, t * (int64_t)H + h);
-                float scaled = xv / s[b];
+                float scaled = copysignf(xv / s[b], xv);   /* s > 0: changes only a NaN's sign */
                 q[h] = e4m3_from_float(scaled);
             }
         }

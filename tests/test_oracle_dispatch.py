@@ -167,6 +167,33 @@ def test_fp8_special_blocks():
     assert np.all(d["recv"][1, 129:] == 0)
 
 
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_fp8_infinite_and_nan_elements(x_dtype):
+    """Hand-derived codes for blocks with infinities and NaNs. amax skips NaN elements; an
+    infinite amax gives s = inf, so finite elements quantise to a signed zero and an infinite one
+    to the NaN code, with the sign of x (a NaN quotient keeps the sign of x, as every quotient by
+    the positive scale does); an all-NaN block has amax 0 and s = 1."""
+    nan, neg_nan = np.float32(np.nan), np.copysign(np.float32(np.nan), np.float32(-1.0))
+    inf = np.float32(np.inf)
+    x = np.zeros((1, 384), np.float32)
+    x[0, :128] = 1.0
+    x[0, :8] = [inf, -inf, 3.0, -3.0, 0.0, -0.0, nan, neg_nan]
+    x[0, 128:132] = [nan, neg_nan, 2.0, -7.0]
+    x[0, 256:384:2], x[0, 257:384:2] = nan, neg_nan
+    xin = x if x_dtype == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16)
+    d = oracle.dispatch(xin, x_dtype, np.array([[0]], np.int32), 1, 1, "fp8_e4m3")
+    s = d["recv_scales"][0]
+    assert np.isinf(s[0]) and s[0] > 0
+    assert s[1] == np.float32(2.0 ** -6)           # 7 / 448
+    assert s[2] == np.float32(1.0)
+    q = d["recv"][0]
+    assert q[:8].tolist() == [0x7F, 0xFF, 0x00, 0x80, 0x00, 0x80, 0x7F, 0xFF]
+    assert np.all(q[8:128] == 0x00)                # 1 / inf = +0
+    assert q[128:132].tolist() == [0x7F, 0xFF, 0x70, 0xFE]   # 128 = 2^7: exponent field 14
+    assert np.all(q[132:256] == 0x00)
+    assert np.all(q[256:384:2] == 0x7F) and np.all(q[257:384:2] == 0xFF)
+
+
 def test_rejects_invalid():
     x = np.zeros((2, 128), np.float32)
     with pytest.raises(ValueError):   # expert id out of range

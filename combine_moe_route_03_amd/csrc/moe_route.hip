@@ -1548,10 +1548,12 @@ __device__ __forceinline__ float quantise8_e4m3(const float (&v)[8], u32x2& pack
             d[i] = copysignf(fmaf(fmaf(-q0, s_up, a * up), r_down, q0), v[i]);
         }
     } else {
+        // s > 0, so a quotient has the sign of v; that of a NaN quotient (an infinite v over an
+        // infinite s) is left open by IEEE 754 and taken from v as well
         uint32_t q[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            q[i] = f32_to_e4m3(v[i] / s);
+            q[i] = f32_to_e4m3(copysignf(v[i] / s, v[i]));
         packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
         packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
         return s;

@@ -122,7 +122,8 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, 
  *   payload_dtype == MOE_FP8_E4M3 ("block-scaled fp8-dispatch", read as 1 x 128 blocks): for every
  *     token and block b of 128 elements, amax = max |x| over the elements that are not NaN,
  *     s = amax / 448 in fp32 (1 when amax = 0), code = e4m3 of the fp32 quotient x / s rounded to
- *     nearest even and saturated to +-448 (a NaN element: the NaN code 0x7F with its sign);
+ *     nearest even and saturated to +-448; a NaN quotient gives the NaN code 0x7F with the sign of
+ *     x (a NaN element, or an infinite one in a block whose s is infinite);
  *     recv [R, H] uint8 codes, recv_scales [R, H/128] fp32 s. Requires H % 128 == 0.
  *   recv 16-byte aligned, recv_scales 4-byte aligned.
  */

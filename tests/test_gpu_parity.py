@@ -388,16 +388,16 @@ def test_fp8_special_blocks():
 
 
 def _quantiser_sweep_x(x_dtype: str, T_min: int, H: int = 4096) -> np.ndarray:
-    """Blocks of 128 that pair every bf16 value (NaN included, infinities excluded) with a set of
+    """Blocks of 128 that pair every bf16 value (NaN and the infinities included) with a set of
     block maxima: each block holds one maximum A (either sign) and 127 values of magnitude at most
     |A|, at shuffled positions. The maxima reach every case of the quantiser: s subnormal, s at the
-    bottom of the normal range, ordinary scales, amax of 2^126 and above 2^127. For f32 x, blocks of
-    random full-precision values at each maximum are added. Rows past the blocks are N(0, 1)."""
+    bottom of the normal range, ordinary scales, amax of 2^126 and above 2^127, and an infinite amax
+    (s = inf: signed zeros, and the NaN code for the infinities). For f32 x, blocks of random
+    full-precision values at each maximum are added. Rows past the blocks are N(0, 1)."""
     rng = np.random.default_rng(11)
     vals = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
-    vals = vals[~np.isinf(vals)]
     maxima = np.array([2.0 ** -133, 2.0 ** -126, 1e-36, 5.3e-36, 1e-30, 2.0 ** -117, 1e-5, 0.37,
-                       1.0, 3.0, 448.0, 1e4, 2.0 ** 126, 3.0e38], np.float32)
+                       1.0, 3.0, 448.0, 1e4, 2.0 ** 126, 3.0e38, np.inf], np.float32)
     maxima = (oracle.f32_to_bf16(maxima).astype(np.uint32) << 16).view(np.float32)
     blocks = []
     for a in maxima:
@@ -405,7 +405,7 @@ def _quantiser_sweep_x(x_dtype: str, T_min: int, H: int = 4096) -> np.ndarray:
         rng.shuffle(sel)
         nb = -(-sel.size // 127)
         sel = np.concatenate([sel, np.zeros(nb * 127 - sel.size, np.float32)]).reshape(nb, 127)
-        if x_dtype == "f32":
+        if x_dtype == "f32" and np.isfinite(a):
             rnd = (rng.uniform(-1.0, 1.0, (64, 127)) * a).astype(np.float32)
             sel = np.concatenate([sel, rnd])
         first = np.where(rng.random(sel.shape[0]) < 0.5, -a, a).astype(np.float32)

@@ -209,3 +209,66 @@ def test_ep_combine_with_pre_reduction(name):
         else:
             assert_close_out(got, want, w.dtype)
     assert o_pc.sum() < S * T * k                                   # fewer rows travel back
+
+
+def test_ep_pre_reduction_special_values():
+    """Expert outputs holding +-inf, NaN, the largest bf16 values and subnormals through the
+    pre-reducing return: the partial rows, and the source-side finish from the oracle's partial
+    rows, match the oracle within one bf16 code, with NaN (the quiet NaN 0x7FC0 on both sides)
+    exactly where the oracle has it."""
+    from gpu_util import bf16_ulp_distance
+    w = EpWorkload("ep_mid", 4, 300, 512, 64, 4, 8, "bf16")
+    _announce("ep pre-reduced combine, special values")
+    c = _run(w)
+    S, N, T = w.S, w.N, w.T
+    pcap = T
+    rng = np.random.default_rng(9)
+    special = oracle.f32_to_bf16(np.array([np.inf, -np.inf, np.nan, 3.3e38, -3.3e38, 1e-40,
+                                           -1e-40], np.float32))
+    ys = []
+    for r in range(N):
+        y = c["o_y"][r].copy()
+        pick = rng.random(y.shape) < 0.02
+        y[pick] = rng.choice(special, size=int(pick.sum()))
+        ys.append(y)
+    # oracle
+    o_pc = np.zeros((N, S), np.int32)
+    o_prow = [oracle.ep_partial_rows(c["idx"][s * T:(s + 1) * T], w.E, N, s, S, pcap, o_pc)
+              for s in range(S)]
+    o_part = np.zeros((N * S * pcap, w.H), np.uint16)
+    for r in range(N):
+        oracle.ep_reduce(ys[r], w.dtype, w.E, N, r, S, w.cap, c["o_recv"][r]["grouped_src"],
+                         c["idx"], c["wt"], np.concatenate(c["o_rows"]), np.concatenate(o_prow),
+                         o_part)
+    o_fin = [oracle.ep_combine_reduced(o_part, w.dtype, o_prow[s], w.dtype) for s in range(S)]
+    # GPU
+    pc = torch.full((N, S), -3, dtype=torch.int32, device="cuda")
+    prow = []
+    for s in range(S):
+        p = torch.empty((T, N), dtype=torch.int32, device="cuda")
+        moe.moe_ep_partial_rows(c["idx_d"][s * T:(s + 1) * T], w.E, N, s, S, pcap, p, pc)
+        prow.append(p)
+    prow_all, rows_all = torch.cat(prow), torch.cat(c["rows"])
+    part = torch.zeros((N * S * pcap, w.H), dtype=torch.bfloat16, device="cuda")
+    ws = moe.moe_ep_reduce_workspace(S, w.cap)
+    for r in range(N):
+        moe.moe_ep_reduce(to_dev(ys[r], w.dtype), w.E, N, r, S, w.cap, c["recv"][r][3],
+                          c["idx_d"], c["w_d"], rows_all, prow_all, pcap, part, ws)
+    part_o = to_dev(o_part, w.dtype)
+    fin_o = [torch.empty((T, w.H), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    for s in range(S):
+        moe.moe_ep_combine_reduced(part_o, prow[s], fin_o[s])
+    torch.cuda.synchronize()
+    g_part = to_host(part)
+    nan_code = 0x7FC0
+    n_special = 0
+    for s in range(S):
+        valid = o_prow[s][o_prow[s] >= 0]
+        got, want = g_part[valid], o_part[valid]
+        assert np.array_equal(got == nan_code, want == nan_code)
+        assert bf16_ulp_distance(got, want).max() <= 1
+        n_special += int((((want & 0x7F80) == 0x7F80)).sum())
+        fg, fw = to_host(fin_o[s]), o_fin[s]
+        assert np.array_equal(fg == nan_code, fw == nan_code)
+        assert bf16_ulp_distance(fg, fw).max() <= 1
+    assert n_special > 100                                           # infinities and NaNs met

@@ -15,7 +15,8 @@
  * Conventions for every entry point:
  *   - Every pointer argument is a DEVICE pointer, except `out` of the dispatch calls, which is a
  *     HOST pointer to a struct of device pointers. The caller allocates and owns every buffer; the
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no state between calls (the one exception,
+ *     moe_route_dispatch_noalloc, keeps a fixed workspace array per device; see there).
  *   - Work is enqueued on `stream` (0 = the null stream); calls return without synchronising.
  *   - All arguments are validated before any launch. On an error status nothing is enqueued and
  *     no output is written. MOE_ERR_HIP means a launch failed (hipGetLastError after the launch).

@@ -38,6 +38,11 @@ MUTANTS = {
         "    if (a->token != b->token) return a->token < b->token ? -1 : 1;",
         "test_oracle_dispatch.py"),
     "fnuz_fp8_max": ("amax / 448.0f", "amax / 240.0f", "test_oracle_dispatch.py"),
+    "fp8_amax_takes_nan": ("if (a > amax)\n                    amax = a;",
+                           "if (!(a <= amax))\n                    amax = a;",
+                           "test_oracle_dispatch.py"),
+    "fp8_nan_quotient_sign_unset": ("float scaled = copysignf(xv / s[b], xv);",
+                                    "float scaled = xv / s[b];", "test_oracle_dispatch.py"),
     "e4m3_subnormal_edge": ("if (ex < -6) ", "if (ex < -7) ", "test_oracle_formats.py"),
     "ties_away_from_zero": ("return nearbyint(a / quantum) * quantum;",
                             "return round(a / quantum) * quantum;", "test_oracle_formats.py"),

@@ -25,10 +25,11 @@
 //                    non-temporal store per lane; token order: one wavefront per (token, 1 KB
 //                    piece), one load stored to all k rows; the pieces of a row run side by side;
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
-//   k_layout_pack    batches of up to 512 tokens: every workgroup rebuilds the whole layout in
-//                    LDS from the ids (LDS counts, one block scan, token bit masks for the ranks)
-//                    and packs its pieces, so layout and packing take one launch; up to 32 routed
-//                    tokens every workgroup also routes the batch itself, so dispatch is one launch;
+//   k_layout_pack    batches of up to 512 tokens (896 for row copies): every workgroup rebuilds
+//                    the whole layout in LDS from the ids (LDS counts, one block scan, token bit
+//                    masks for the ranks) and packs its pieces, so layout and packing take one
+//                    launch; up to 32 routed tokens every workgroup also routes the batch itself,
+//                    so dispatch is one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
 //                    fp32 fused multiply-adds, one 16-byte non-temporal store per 8 outputs;
 //   k_ep_recv_plan   expert-parallel receive: every workgroup scans a rank's per-(source, expert)
@@ -67,7 +68,9 @@ constexpr int kLpThreads = 512;          //   (8 wavefronts a workgroup, two exp
 constexpr int kLpWaves = kLpThreads / 64;
 constexpr int kLpMaxGroups = 1024;       //   (grid-stride beyond this many workgroups)
 constexpr int kLpWideThreads = 1024;     //   above kLpWideTokens tokens, 16 wavefronts a
-constexpr int kLpWideTokens = 256;       //   workgroup (row copies without routing)
+constexpr int kLpWideTokens = 256;       //   workgroup (row copies without routing),
+constexpr int kLpCopyTokens = 896;       //   up to this many tokens for row copies,
+constexpr int kLpWideMaxGroups = 512;    //   at most one round of them (two on each of 256 CUs)
 constexpr int kLpRouteTokens = kLpThreads / 16;   // routing in the same launch: at most 32 tokens
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -1606,9 +1609,10 @@ __global__ __launch_bounds__(64 * kPackWaves) void k_pack_rows_fp8(
 }
 
 // ------------------------------------------------------------- layout and packing in one launch --
-// Layout and packing of a batch of at most kLpTokens tokens in one launch: at these sizes every
-// launch costs more than its work, so the scan and row kernels are folded into the packing. Every
-// workgroup rebuilds the whole layout in LDS from the T*k expert ids (read from L2):
+// Layout and packing of a batch of at most kLpTokens tokens (kLpCopyTokens for row copies) in one
+// launch: at these sizes every launch costs more than its work, so the scan and row kernels are
+// folded into the packing. Every workgroup rebuilds the whole layout in LDS from the T*k expert ids
+// (read from L2):
 //   - counts: one LDS atomic add per slot (order does not matter for a count); one block scan turns
 //     them into expert offsets;
 //   - ranks: token t sets bit t % 32 of word t / 32 of the mask of each of its experts. When no
@@ -2644,16 +2648,18 @@ void launch_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H, int32
                                                                pp, rv, recv_scales);
 }
 
-// Layout (and packing, unless payload is null) of a batch in one launch: up to kLpTokens tokens,
-// with the masks and offsets in 64 KB of LDS.
+// Layout (and packing, unless payload is null) of a batch in one launch: up to kLpTokens tokens
+// (kLpCopyTokens for row copies), with the masks and offsets in 64 KB of LDS.
 inline size_t lp_lds_bytes(int32_t T, int32_t E)
 {
     return ((size_t)ceil_div(T, 32) * E + E + 1) * sizeof(uint32_t);
 }
 
-inline bool lp_fits(int32_t T, int32_t E)
+// copy: the payload is x's own bytes (row copies take the one-launch layout up to kLpCopyTokens).
+inline bool lp_fits(int32_t T, int32_t E, bool copy = false)
 {
-    return T >= 1 && T <= kLpTokens && lp_lds_bytes(T, E) + 256 <= 64 * 1024;   // + static LDS
+    return T >= 1 && T <= (copy ? kLpCopyTokens : kLpTokens) &&
+           lp_lds_bytes(T, E) + 256 <= 64 * 1024;        // + static LDS
 }
 
 // Routing in the same launch as layout and packing: small batches of routed tokens.
@@ -2730,9 +2736,11 @@ void launch_layout_pack(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t H
         // at hidden 7168 bf16, E 256, k 8 (µs per step): 384 tokens 27.05 -> 26.7, 512 tokens
         // 34.2 -> 32.6, 256 and fewer unchanged or slower. The fp8 modes keep 8 wavefronts: their
         // quantising workgroups ran 24.2 -> 28.0 us at 384 tokens (fewer, longer workgroups than
-        // CUs can take in one round).
+        // CUs can take in one round). The grid stays within one round of workgroups (wavefronts
+        // take further units in turn): a second round rebuilds the layout again, 42.9 -> 40.3 us
+        // at 640 tokens; with it, row copies take this launch up to 896 tokens.
         const int64_t groups16 = ceil_div((int64_t)T * lp.pieces, kLpWideThreads / 64);
-        const dim3 grid16((unsigned)(groups16 < kLpMaxGroups ? groups16 : kLpMaxGroups));
+        const dim3 grid16((unsigned)(groups16 < kLpWideMaxGroups ? groups16 : kLpWideMaxGroups));
         k_layout_pack<LP_COPY, 0, kLpWideThreads><<<grid16, kLpWideThreads, lds, stream>>>(lp, co);
         return;
     }
@@ -2877,7 +2885,7 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
         return MOE_ERR_WORKSPACE;
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
-    if (lp_fits(T, E)) {
+    if (lp_fits(T, E, payload_dtype != MOE_FP8_E4M3)) {
         launch_layout_pack(x, x_dtype, T, H, E, k, topk_idx, &payload_dtype, out,
                            count_outputs(out, n_ranks), stream);
         return launch_status();
@@ -2930,7 +2938,7 @@ moe_status_t route_dispatch(const float* logits, const void* x, moe_dtype_t x_dt
                            count_outputs(out, n_ranks), stream, nullptr, logits, topk_w);
         return launch_status();
     }
-    if (lp_fits(T, E)) {
+    if (lp_fits(T, E, payload_dtype != MOE_FP8_E4M3)) {
         // small batches: routing, then layout and packing in one launch
         launch_route(logits, T, E, k, topk_idx, topk_w, stream);
         launch_layout_pack(x, x_dtype, T, H, E, k, topk_idx, &payload_dtype, out,

@@ -212,14 +212,14 @@ EDGE = [
     (16401, 128, 64, 2, 4, "f32", "f32"),       # one token more: separate route + histogram
     # the multi-launch layout reads x ahead in its launches (thirds, or halves when routing takes a
     # wavefront a token); every part must stay inside x
-    (700, 2056, 64, 4, 8, "bf16", "bf16"),      # a wavefront a token (T < 1024), ragged row tail
+    (900, 2056, 64, 4, 8, "bf16", "bf16"),      # a wavefront a token (T < 1024), ragged row tail
     (1100, 256, 384, 20, 48, "f32", "f32"),     # k > 16 past 1024 tokens
     (1024, 1024, 256, 8, 32, "bf16", "fp8_e4m3"),   # fp8 packing after the multi-launch layout
     # routed rows from the byte-count table (two layout launches): E padded to 16 in the table,
     # a partial last block; and many windows of few blocks with fp8 from fp32
     (1500, 264, 100, 6, 5, "bf16", "bf16"),
     (2100, 128, 520, 4, 8, "f32", "fp8_e4m3"),
-    # layout folded into packing (up to 512 tokens through moe_route_dispatch)
+    # layout folded into packing (up to 512 tokens, 896 for row copies)
     (100, 4104, 64, 4, 8, "bf16", "bf16"),      # ragged 16-byte tail, tokens across 4 mask words
     (200, 256, 384, 32, 48, "f32", "f32"),      # k > 16 (a wavefront a token in routing)
     (129, 512, 8, 8, 2, "bf16", "bf16"),        # k = E: every token on every expert
@@ -227,8 +227,12 @@ EDGE = [
     (256, 1024, 1024, 64, 8, "f32", "fp8_e4m3"),    # k at its maximum, fp8 from fp32
     (448, 512, 1024, 2, 4, "bf16", "bf16"),     # most tokens that fit 64 KB of masks at E = 1024
     (449, 512, 1024, 2, 4, "bf16", "bf16"),     # one token more: the multi-launch layout
-    (512, 1536, 256, 8, 32, "bf16", "bf16"),    # most tokens the one-launch layout takes
-    (513, 512, 64, 2, 4, "bf16", "bf16"),       # one token more: the multi-launch layout
+    (512, 1536, 256, 8, 32, "bf16", "fp8_e4m3"),    # most tokens the one-launch fp8 layout takes
+    (513, 512, 64, 2, 4, "bf16", "fp8_e4m3"),   # one token more: the multi-launch layout
+    (513, 512, 64, 2, 4, "bf16", "bf16"),       # row copies go on in one launch (16 wavefronts)
+    (896, 7168, 256, 8, 32, "bf16", "bf16"),    # most tokens for row copies; more units than one
+                                                # round of workgroups, so wavefronts take several
+    (897, 512, 64, 2, 4, "f32", "f32"),         # one token more: the multi-launch layout
     # routing in the same launch as layout and packing (up to 32 tokens, k <= 16, E <= 256)
     (32, 256, 256, 16, 16, "bf16", "bf16"),     # at every limit
     (33, 256, 256, 16, 16, "f32", "fp8_e4m3"),  # one token more: a separate routing launch
@@ -344,7 +348,8 @@ def test_route_with_one_lane_holding_the_best_experts(T, E, k):
 
 
 @pytest.mark.parametrize("T,H,E,k,N,payload", [
-    (600, 128, 16, 4, 4, "f32"),       # multi-launch layout
+    (1000, 128, 16, 4, 4, "f32"),      # multi-launch layout
+    (700, 128, 16, 4, 4, "f32"),       # one-launch layout of row copies past 512 tokens, exact ranks
     (300, 128, 16, 4, 4, "f32"),       # one-launch layout, exact ranks
     (37, 256, 8, 8, 2, "fp8_e4m3"),    # one-launch layout, k = E with repeats, fp8 from fp32
     (512, 64, 256, 3, 8, "f32"),       # one-launch layout at its token limit, few repeats

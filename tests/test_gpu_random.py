@@ -1,7 +1,7 @@
 """Seeded random shapes through moe_route_dispatch, moe_dispatch (caller ids, some with repeats)
-and moe_combine, against the oracle. Shapes cross the one-launch layout's limits (512 tokens, 64 KB
-of masks), ragged rows and pieces, E up to 1024 and k up to 64; every output is compared bit for
-bit (combine to one bf16 code / 1e-5 relative)."""
+and moe_combine, against the oracle. Shapes cross the one-launch layout's limits (512 tokens, 896
+for row copies, 64 KB of masks), ragged rows and pieces, E up to 1024 and k up to 64; every output
+is compared bit for bit (combine to one bf16 code / 1e-5 relative)."""
 import numpy as np
 import pytest
 import torch

@@ -3177,7 +3177,7 @@ moe_status_t moe_ep_send(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t 
     ep.sources = n_sources;
     ep.cap = cap;
     ep.L = E / n_ranks;
-    if (lp_fits(T, E)) {
+    if (lp_fits(T, E, true)) {
         moe_dispatch_out_t o = {};
         o.recv = regions;
         o.token_row = send_row;

@@ -233,6 +233,8 @@ EDGE = [
     (896, 7168, 256, 8, 32, "bf16", "bf16"),    # most tokens for row copies; more units than one
                                                 # round of workgroups, so wavefronts take several
     (897, 512, 64, 2, 4, "f32", "f32"),         # one token more: the multi-launch layout
+    (300, 16384, 64, 2, 4, "bf16", "bf16"),     # 32 pieces a row: 600 workgroups capped at 512
+    (512, 16384, 64, 2, 4, "bf16", "fp8_e4m3"),     # fp8, 32 pieces: 2048 workgroups capped at 1024
     # routing in the same launch as layout and packing (up to 32 tokens, k <= 16, E <= 256)
     (32, 256, 256, 16, 16, "bf16", "bf16"),     # at every limit
     (33, 256, 256, 16, 16, "f32", "fp8_e4m3"),  # one token more: a separate routing launch

@@ -25,11 +25,11 @@
 //                    non-temporal store per lane; token order: one wavefront per (token, 1 KB
 //                    piece), one load stored to all k rows; the pieces of a row run side by side;
 //   k_pack_rows_fp8  same, quantising 1x128 blocks to e4m3 with an fp32 absmax/448 scale;
-//   k_layout_pack    batches of up to 512 tokens (896 for row copies): every workgroup rebuilds
-//                    the whole layout in LDS from the ids (LDS counts, one block scan, token bit
-//                    masks for the ranks) and packs its pieces, so layout and packing take one
-//                    launch; up to 32 routed tokens every workgroup also routes the batch itself,
-//                    so dispatch is one launch;
+//   k_layout_pack    batches of up to 512 tokens (896 routed ones for row copies): every
+//                    workgroup rebuilds the whole layout in LDS from the ids (LDS counts, one
+//                    block scan, token bit masks for the ranks) and packs its pieces, so layout
+//                    and packing take one launch; up to 32 routed tokens every workgroup also
+//                    routes the batch itself, so dispatch is one launch;
 //   k_combine        one wavefront per (token, 512-element segment): all k row loads in flight,
 //                    fp32 fused multiply-adds, one 16-byte non-temporal store per 8 outputs;
 //   k_ep_recv_plan   expert-parallel receive: every workgroup scans a rank's per-(source, expert)
@@ -69,7 +69,7 @@ constexpr int kLpWaves = kLpThreads / 64;
 constexpr int kLpMaxGroups = 1024;       //   (grid-stride beyond this many workgroups)
 constexpr int kLpWideThreads = 1024;     //   above kLpWideTokens tokens, 16 wavefronts a
 constexpr int kLpWideTokens = 256;       //   workgroup (row copies without routing),
-constexpr int kLpCopyTokens = 896;       //   up to this many tokens for row copies,
+constexpr int kLpCopyTokens = 896;       //   up to this many routed tokens for row copies,
 constexpr int kLpWideMaxGroups = 512;    //   at most one round of them (two on each of 256 CUs)
 constexpr int kLpRouteTokens = kLpThreads / 16;   // routing in the same launch: at most 32 tokens
 
@@ -2655,7 +2655,11 @@ inline size_t lp_lds_bytes(int32_t T, int32_t E)
     return ((size_t)ceil_div(T, 32) * E + E + 1) * sizeof(uint32_t);
 }
 
-// copy: the payload is x's own bytes (row copies take the one-launch layout up to kLpCopyTokens).
+// copy: routed ids (never repeated within a token) whose payload is x's own bytes take the
+// one-launch layout up to kLpCopyTokens. Caller-given ids keep kLpTokens: a token that names an
+// expert twice sends every wavefront through the exact-rank scan of all earlier slots, which grows
+// with T squared (896 tokens with repeats: 144 us a dispatch, against 32 us in the multi-launch
+// layout).
 inline bool lp_fits(int32_t T, int32_t E, bool copy = false)
 {
     return T >= 1 && T <= (copy ? kLpCopyTokens : kLpTokens) &&
@@ -2885,7 +2889,7 @@ moe_status_t moe_dispatch(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t
         return MOE_ERR_WORKSPACE;
     if (!aligned(workspace, 16))
         return MOE_ERR_UNSUPPORTED;
-    if (lp_fits(T, E, payload_dtype != MOE_FP8_E4M3)) {
+    if (lp_fits(T, E)) {
         launch_layout_pack(x, x_dtype, T, H, E, k, topk_idx, &payload_dtype, out,
                            count_outputs(out, n_ranks), stream);
         return launch_status();
@@ -3177,7 +3181,7 @@ moe_status_t moe_ep_send(const void* x, moe_dtype_t x_dtype, int32_t T, int32_t 
     ep.sources = n_sources;
     ep.cap = cap;
     ep.L = E / n_ranks;
-    if (lp_fits(T, E, true)) {
+    if (lp_fits(T, E)) {
         moe_dispatch_out_t o = {};
         o.recv = regions;
         o.token_row = send_row;

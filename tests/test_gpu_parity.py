@@ -229,9 +229,11 @@ EDGE = [
     (449, 512, 1024, 2, 4, "bf16", "bf16"),     # one token more: the multi-launch layout
     (512, 1536, 256, 8, 32, "bf16", "fp8_e4m3"),    # most tokens the one-launch fp8 layout takes
     (513, 512, 64, 2, 4, "bf16", "fp8_e4m3"),   # one token more: the multi-launch layout
-    (513, 512, 64, 2, 4, "bf16", "bf16"),       # row copies go on in one launch (16 wavefronts)
-    (896, 7168, 256, 8, 32, "bf16", "bf16"),    # most tokens for row copies; more units than one
-                                                # round of workgroups, so wavefronts take several
+    (513, 512, 64, 2, 4, "bf16", "bf16"),       # routed row copies go on in one launch (16
+                                                # wavefronts a workgroup); caller ids do not
+    (896, 7168, 256, 8, 32, "bf16", "bf16"),    # most routed tokens for row copies; more units
+                                                # than one round of workgroups, so wavefronts
+                                                # take several
     (897, 512, 64, 2, 4, "f32", "f32"),         # one token more: the multi-launch layout
     (300, 16384, 64, 2, 4, "bf16", "bf16"),     # 32 pieces a row: 600 workgroups capped at 512
     (512, 16384, 64, 2, 4, "bf16", "fp8_e4m3"),     # fp8, 32 pieces: 2048 workgroups capped at 1024
@@ -351,7 +353,7 @@ def test_route_with_one_lane_holding_the_best_experts(T, E, k):
 
 @pytest.mark.parametrize("T,H,E,k,N,payload", [
     (1000, 128, 16, 4, 4, "f32"),      # multi-launch layout
-    (700, 128, 16, 4, 4, "f32"),       # one-launch layout of row copies past 512 tokens, exact ranks
+    (700, 128, 16, 4, 4, "f32"),       # multi-launch layout past 512 tokens (caller ids)
     (300, 128, 16, 4, 4, "f32"),       # one-launch layout, exact ranks
     (37, 256, 8, 8, 2, "fp8_e4m3"),    # one-launch layout, k = E with repeats, fp8 from fp32
     (512, 64, 256, 3, 8, "f32"),       # one-launch layout at its token limit, few repeats

@@ -326,16 +326,18 @@ __device__ __forceinline__ int route_token(const float* __restrict__ l, int32_t 
     return route_token_from<PL>(v, E, k, idx_out, w_out);
 }
 
-// Routing with one whole wavefront per token (any k up to 64).
+// Routing with one whole wavefront per token (any k up to 64), one wavefront a workgroup: the
+// tokens' logit loads go out from as many CUs as there are tokens (128 decode tokens: the step
+// 13.95 -> 13.46 us against four wavefronts a workgroup).
 template <int PL>
-__global__ __launch_bounds__(kThreads) void k_route_topk_wide(const float* __restrict__ logits,
-                                                         int32_t T, int32_t E, int32_t k,
-                                                         int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_w)
+__global__ __launch_bounds__(64) void k_route_topk_wide(const float* __restrict__ logits,
+                                                   int32_t T, int32_t E, int32_t k,
+                                                   int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w)
 {
-    const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t t = blockIdx.x;
     if (t >= T)
-        return;                                          // uniform: whole wavefronts leave
+        return;
     route_token<PL>(logits + t * E, E, k, topk_idx + t * k, topk_w + t * k);
 }
 
@@ -2418,8 +2420,7 @@ void launch_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t*
         const dim3 grid((unsigned)ceil_div(T, kThreads / 16));
         MOE_ROUTE16_LAUNCH(k_route_topk, grid, kThreads, 0, logits, T, E, k, topk_idx, topk_w);
     } else {
-        const dim3 grid((unsigned)ceil_div(T, kWaves));
-        MOE_ROUTE_LAUNCH(k_route_topk_wide, grid, kThreads, 0, logits, T, E, k, topk_idx,
+        MOE_ROUTE_LAUNCH(k_route_topk_wide, dim3((unsigned)T), 64, 0, logits, T, E, k, topk_idx,
                          topk_w);
     }
 }
